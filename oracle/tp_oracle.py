@@ -1,0 +1,315 @@
+"""CPU fp64 oracle for one GPU's tensor-parallel shard of a transformer layer.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this module.  The product path (the HIP library and
+its Python binding) never calls it, and it shares no code with that path.
+
+Everything here is plain numpy float64 on the CPU, written so that each function
+can be checked by eye against the passage it cites:
+
+  [P3] "Understanding Tensor Parallelism for Multi-GPU LLM Serving" (DevBytes),
+       section "How Tensor Parallelism Works Under the Hood" and the
+       ColumnParallelLinear / RowParallelLinear listing of section
+       "Implementing Tensor Parallelism with Hugging Face Accelerate".
+  [P4] "What is tensor parallelism?" (tecyfy), section "How a layer is split".
+  [P5] "Tensor parallel serving" (Learn AI), the simulation script of section
+       "Simulating the split, and proving it is correct", its "Line-by-line
+       walkthrough", "Common mistakes", "Try it yourself" and the researcher
+       section "Column-parallel and row-parallel layers, paired".
+
+Inputs are arrays of stored values (bf16 or fp32); they are widened exactly to
+float64 and every intermediate stays float64 and unrounded.
+
+Conventions (readings where the pages leave a step open):
+  * A weight is stored [out_features, in_features] row-major, as the listing
+    stores it; the pages' Y = XW is therefore computed as X @ W^T (+ b), the
+    form the simulation script uses.
+  * Shard r of p owns the contiguous block [r*n/p, (r+1)*n/p) of the split
+    dimension; concat and sum run in rank order.
+  * SwiGLU is silu(X Wg^T + bg) * (X Wu^T + bu), silu(z) = z / (1 + exp(-z)).
+    The pages never define it (they show GELU); this is the usual gated form.
+  * Head split of a fused QKV weight: shard r owns Q heads
+    [r*H/p, (r+1)*H/p) and KV heads [r*G/p, (r+1)*G/p) (GQA is not on the
+    pages; this is the plain reading of "different attention heads go to
+    different GPUs" with the TP size dividing the head counts).
+
+Parity status per function (what pins it, beside itself):
+  linear, col_shard, row_shard, concat, combine_sum:  pinned (printed toy
+      output, brute-force fsum, closed-form special cases, page invariants).
+  silu / swiglu:  pinned by closed forms of the definition; the choice of
+      SwiGLU over GELU is a reading.
+  qkv head layout / attention stand-in (A := Q):  parity unpinned by the
+      pages (self-consistency invariants only).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def f64(a) -> np.ndarray:
+    """Exact widening of stored values to float64."""
+    return np.asarray(a, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# The linear layer Y = XW  ([P3] "How Tensor Parallelism Works Under the Hood";
+# [P5] simulation script: full_output = x @ W.T + b)
+# ---------------------------------------------------------------------------
+
+def linear(x, w, b=None) -> np.ndarray:
+    """Y[m, n] = sum_k X[m, k] * W[n, k] (+ b[n]), W stored [out, in]."""
+    y = f64(x) @ f64(w).T
+    if b is not None:
+        y = y + f64(b)[None, :]
+    return y
+
+
+def linear_fsum(x, w, b=None) -> np.ndarray:
+    """The same definition with explicit loops and an exactly rounded sum.
+
+    Products of two bf16 or fp32 values are exact in float64, so math.fsum
+    returns the correctly rounded dot product.  For tiny inputs only.
+    """
+    x, w = f64(x), f64(w)
+    m_count, k_count = x.shape
+    n_count = w.shape[0]
+    y = np.empty((m_count, n_count))
+    for m in range(m_count):
+        for n in range(n_count):
+            terms = [x[m, k] * w[n, k] for k in range(k_count)]
+            if b is not None:
+                terms.append(float(f64(b)[n]))
+            y[m, n] = math.fsum(terms)
+    return y
+
+
+def linear_entry(x_row, w_row, b_n=None) -> float:
+    """One output entry by fsum: for spot checks of large shapes."""
+    terms = list(f64(x_row) * f64(w_row))
+    if b_n is not None:
+        terms.append(float(b_n))
+    return math.fsum(terms)
+
+
+# ---------------------------------------------------------------------------
+# Sharding ([P3] listing: out_features // world_size rows per rank for the
+# column layer, in_features // world_size inputs for the row layer, both
+# asserted divisible; [P5] W[:split], W[split:])
+# ---------------------------------------------------------------------------
+
+def _block(n: int, p: int, r: int) -> slice:
+    if p <= 0 or n % p != 0:
+        raise ValueError(f"size {n} is not divisible by tensor_parallel_size {p}")
+    if not 0 <= r < p:
+        raise ValueError(f"rank {r} outside [0, {p})")
+    step = n // p
+    return slice(r * step, (r + 1) * step)
+
+
+def col_shard(w, b, p: int, r: int):
+    """Column-parallel shard r: the block of output rows W[r*N/p:(r+1)*N/p, :] and b likewise."""
+    s = _block(np.shape(w)[0], p, r)
+    return f64(w)[s, :], (None if b is None else f64(b)[s])
+
+
+def col_shard_uneven(w, b, widths):
+    """Column split into consecutive blocks of the given widths ([P5] "Try it yourself")."""
+    out, start = [], 0
+    for width in widths:
+        out.append((f64(w)[start:start + width, :],
+                    None if b is None else f64(b)[start:start + width]))
+        start += width
+    if start != np.shape(w)[0]:
+        raise ValueError("widths do not cover the output features")
+    return out
+
+
+def row_shard(w, p: int, r: int) -> np.ndarray:
+    """Row-parallel shard r: the block of input columns W[:, r*K/p:(r+1)*K/p]."""
+    s = _block(np.shape(w)[1], p, r)
+    return f64(w)[:, s]
+
+
+def input_slice(x, p: int, r: int) -> np.ndarray:
+    """x[..., r*K/p:(r+1)*K/p], the slice the row layer takes by rank ([P3] RowParallelLinear.forward)."""
+    s = _block(np.shape(x)[1], p, r)
+    return f64(x)[:, s]
+
+
+# ---------------------------------------------------------------------------
+# Per-shard products
+# ---------------------------------------------------------------------------
+
+def col_linear(x, w_r, b_r=None) -> np.ndarray:
+    """Y_r = X W_r (+ b_r): full, replicated input; a slice of the output ([P3], [P5])."""
+    return linear(x, w_r, b_r)
+
+
+def row_partial(x_r, w_r) -> np.ndarray:
+    """P_r = X_r W_r with no bias: a partial sum of the full output ([P3])."""
+    return linear(x_r, w_r, None)
+
+
+# ---------------------------------------------------------------------------
+# Combines ([P5] torch.cat([...], dim=-1); [P3] all_reduce(SUM) then + bias;
+# [P5] "Common mistakes": row-parallel combines by summing, not concatenating)
+# ---------------------------------------------------------------------------
+
+def concat(shards, seg_widths=None) -> np.ndarray:
+    """Concatenate per-shard outputs along the feature axis, in rank order.
+
+    With seg_widths = (w_0, ..., w_{s-1}) each shard holds s segments side by
+    side; segment j of every shard is gathered into output block j, shards in
+    rank order inside the block (used for the fused Q|K|V output).
+    """
+    shards = [f64(s) for s in shards]
+    if seg_widths is None:
+        return np.concatenate(shards, axis=-1)
+    blocks = []
+    start = 0
+    for width in seg_widths:
+        blocks.append(np.concatenate([s[:, start:start + width] for s in shards], axis=-1))
+        start += width
+    return np.concatenate(blocks, axis=-1)
+
+
+def combine_sum(partials, b=None) -> np.ndarray:
+    """Y = sum_r P_r, ranks ascending, then + b once."""
+    acc = np.zeros_like(f64(partials[0]))
+    for p_r in partials:
+        acc = acc + f64(p_r)
+    if b is not None:
+        acc = acc + f64(b)[None, :]
+    return acc
+
+
+# ---------------------------------------------------------------------------
+# Activation between the paired layers
+# ---------------------------------------------------------------------------
+
+def silu(z) -> np.ndarray:
+    """silu(z) = z * sigmoid(z) = z / (1 + exp(-z))."""
+    z = f64(z)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def swiglu(g, u) -> np.ndarray:
+    """H = silu(G) * U, elementwise."""
+    return silu(g) * f64(u)
+
+
+# ---------------------------------------------------------------------------
+# Paired column -> row MLP ([P3] "How Tensor Parallelism Works Under the Hood":
+# first layer column-parallel, second row-parallel; [P5] researcher section:
+# the intermediate between them is never communicated)
+# ---------------------------------------------------------------------------
+
+def mlp(x, wg, wu, wd, bg=None, bu=None, bd=None):
+    """Unsharded SwiGLU MLP: Y = (silu(X Wg^T + bg) * (X Wu^T + bu)) Wd^T + bd."""
+    h = swiglu(linear(x, wg, bg), linear(x, wu, bu))
+    return linear(h, wd, bd)
+
+
+def mlp_shard(x, wg_r, wu_r, wd_r, bg_r=None, bu_r=None):
+    """Shard r of the MLP: H_r from the column pair, P_r = H_r Wd_r^T (no bias)."""
+    h_r = swiglu(col_linear(x, wg_r, bg_r), col_linear(x, wu_r, bu_r))
+    return h_r, row_partial(h_r, wd_r)
+
+
+def mlp_shards(x, wg, wu, wd, p, bg=None, bu=None):
+    """All p shards, from slices of the unsharded weights."""
+    out = []
+    for r in range(p):
+        wg_r, bg_r = col_shard(wg, bg, p, r)
+        wu_r, bu_r = col_shard(wu, bu, p, r)
+        wd_r = row_shard(wd, p, r)
+        out.append(mlp_shard(x, wg_r, wu_r, wd_r, bg_r, bu_r))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Head-split attention projections ([P4] "How a layer is split": heads go to
+# different GPUs; the TP size divides the heads; [P5] one all-reduce per
+# attention block)
+# ---------------------------------------------------------------------------
+
+def qkv_rows(n_heads, n_kv_heads, head_dim, p, r):
+    """Row indices of the fused [Wq; Wk; Wv] weight owned by shard r, in order Q | K | V."""
+    if n_heads % p or n_kv_heads % p:
+        raise ValueError("tensor_parallel_size must divide the head counts")
+    hq, hk = n_heads // p, n_kv_heads // p
+    d = head_dim
+    q = np.arange(r * hq * d, (r + 1) * hq * d)
+    k0 = n_heads * d
+    k = np.arange(k0 + r * hk * d, k0 + (r + 1) * hk * d)
+    v0 = (n_heads + n_kv_heads) * d
+    v = np.arange(v0 + r * hk * d, v0 + (r + 1) * hk * d)
+    return np.concatenate([q, k, v])
+
+
+def qkv_shard(wqkv, bqkv, n_heads, n_kv_heads, head_dim, p, r):
+    rows = qkv_rows(n_heads, n_kv_heads, head_dim, p, r)
+    return f64(wqkv)[rows, :], (None if bqkv is None else f64(bqkv)[rows])
+
+
+def qkv_segments(n_heads, n_kv_heads, head_dim, p):
+    """Per-shard segment widths of the fused output: (Q, K, V)."""
+    return (n_heads // p * head_dim, n_kv_heads // p * head_dim, n_kv_heads // p * head_dim)
+
+
+def attn_proj_shard(x, wqkv_r, bqkv_r, a_r, wo_r):
+    """QKV_r = X Wqkv_r^T + bqkv_r (column); P_r = A_r Wo_r^T (row partial)."""
+    qkv_r = None if wqkv_r is None else col_linear(x, wqkv_r, bqkv_r)
+    p_r = None if wo_r is None else row_partial(a_r, wo_r)
+    return qkv_r, p_r
+
+
+# ---------------------------------------------------------------------------
+# Full layer chain with the attention-core stand-in A := Q (a reading: the core
+# is not on the pages).  X -> QKV -> A := Q -> Y1 = sum_r O-partials + bo
+#   -> Y = sum_r MLP-partials(Y1) + bd.   No residual, no norm.
+# ---------------------------------------------------------------------------
+
+def layer_unsharded(x, w):
+    """w: dict with Wqkv, bqkv, Wo, bo, Wg, bg, Wu, bu, Wd, bd and n_heads, n_kv_heads, head_dim."""
+    nq = w["n_heads"] * w["head_dim"]
+    qkv = linear(x, w["Wqkv"], w.get("bqkv"))
+    a = qkv[:, :nq]
+    y1 = linear(a, w["Wo"], w.get("bo"))
+    return mlp(y1, w["Wg"], w["Wu"], w["Wd"], w.get("bg"), w.get("bu"), w.get("bd"))
+
+
+def layer_sharded(x, w, p):
+    """The same chain computed shard by shard and combined (column, row, sum, concat)."""
+    nh, nkv, d = w["n_heads"], w["n_kv_heads"], w["head_dim"]
+    qkv_parts, o_parts = [], []
+    for r in range(p):
+        wqkv_r, bqkv_r = qkv_shard(w["Wqkv"], w.get("bqkv"), nh, nkv, d, p, r)
+        qkv_r = col_linear(x, wqkv_r, bqkv_r)
+        a_r = qkv_r[:, : nh // p * d]
+        o_parts.append(row_partial(a_r, row_shard(w["Wo"], p, r)))
+        qkv_parts.append(qkv_r)
+    y1 = combine_sum(o_parts, w.get("bo"))
+    mlp_parts = mlp_shards(y1, w["Wg"], w["Wu"], w["Wd"], p, w.get("bg"), w.get("bu"))
+    y = combine_sum([pr for _, pr in mlp_parts], w.get("bd"))
+    qkv = concat(qkv_parts, qkv_segments(nh, nkv, d, p))
+    h = concat([h_r for h_r, _ in mlp_parts])
+    return {"qkv": qkv, "y1": y1, "h": h, "y": y}
+
+
+# ---------------------------------------------------------------------------
+# Error metric: e = max|y - y_ref| / max|y_ref| (absolute when y_ref is all zero)
+# ---------------------------------------------------------------------------
+
+def rel_err(y, y_ref) -> float:
+    y, y_ref = f64(y), f64(y_ref)
+    if y.shape != y_ref.shape:
+        raise ValueError(f"shape {y.shape} != {y_ref.shape}")
+    if y.size == 0:
+        return 0.0
+    num = float(np.max(np.abs(y - y_ref)))
+    den = float(np.max(np.abs(y_ref)))
+    return num / den if den > 0 else num

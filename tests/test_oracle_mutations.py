@@ -1,0 +1,100 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that a pin catches each.
+
+Each mutation replaces one oracle function with a wrong variant; the listed pin
+tests must then fail.  This shows the pins are sensitive to dropped terms,
+wrong signs or indices, and transposed or misplaced operands.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.tp_oracle as T
+import test_oracle_pins as P
+
+
+def _patch(monkeypatch, name, fn):
+    monkeypatch.setattr(T, name, fn)
+    monkeypatch.setattr(oracle, name, fn)
+
+
+def _linear_no_bias(x, w, b=None):
+    return T.f64(x) @ T.f64(w).T
+
+
+def _linear_bias_twice(x, w, b=None):
+    y = T.f64(x) @ T.f64(w).T
+    return y if b is None else y + 2 * T.f64(b)[None, :]
+
+
+def _silu_wrong_sign(z):
+    z = T.f64(z)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(z))
+
+
+def _silu_sigmoid_only(z):
+    z = T.f64(z)
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-z))
+
+
+def _combine_sum_bias_each(partials, b=None):
+    acc = np.zeros_like(T.f64(partials[0]))
+    for p_r in partials:
+        acc = acc + T.f64(p_r) + (0 if b is None else T.f64(b)[None, :])
+    return acc
+
+
+def _combine_sum_drop_last(partials, b=None):
+    acc = np.zeros_like(T.f64(partials[0]))
+    for p_r in partials[:-1]:
+        acc = acc + T.f64(p_r)
+    return acc if b is None else acc + T.f64(b)[None, :]
+
+
+def _col_shard_off_by_one(w, b, p, r):
+    n = np.shape(w)[0]
+    step = n // p
+    s = slice(r * step + (1 if r else 0), (r + 1) * step + (1 if r and (r + 1) * step < n else 0))
+    return T.f64(w)[s, :], (None if b is None else T.f64(b)[s])
+
+
+def _row_shard_wrong_axis(w, p, r):
+    n = np.shape(w)[0]
+    step = n // p
+    return T.f64(w)[r * step:(r + 1) * step, :]
+
+
+def _concat_reversed(shards, seg_widths=None):
+    return np.concatenate([T.f64(s) for s in shards[::-1]], axis=-1)
+
+
+def _qkv_rows_shared_kv(n_heads, n_kv_heads, head_dim, p, r):
+    hq, hk, d = n_heads // p, n_kv_heads // p, head_dim
+    q = np.arange(r * hq * d, (r + 1) * hq * d)
+    k = np.arange(n_heads * d, n_heads * d + hk * d)            # always KV head block 0
+    v = np.arange((n_heads + n_kv_heads) * d, (n_heads + n_kv_heads) * d + hk * d)
+    return np.concatenate([q, k, v])
+
+
+MUTATIONS = [
+    ("linear", _linear_no_bias, [P.test_toy_full_output_matches_printed_values]),
+    ("linear", _linear_bias_twice, [P.test_toy_full_output_matches_printed_values,
+                                    P.test_identity_weight_returns_input_plus_bias]),
+    ("silu", _silu_wrong_sign, [P.test_silu_closed_forms, P.test_mlp_tiny_by_bruteforce]),
+    ("silu", _silu_sigmoid_only, [P.test_silu_closed_forms, P.test_swiglu_special_cases]),
+    ("combine_sum", _combine_sum_bias_each, [P.test_toy_row_split_sum_plus_bias_equals_unsharded]),
+    ("combine_sum", _combine_sum_drop_last, [P.test_toy_row_split_sum_plus_bias_equals_unsharded]),
+    ("col_shard", _col_shard_off_by_one, [P.test_toy_column_split_concat_matches_printed_values_and_is_exact]),
+    ("row_shard", _row_shard_wrong_axis, [P.test_toy_row_split_sum_plus_bias_equals_unsharded]),
+    ("concat", _concat_reversed, [P.test_toy_column_split_concat_matches_printed_values_and_is_exact]),
+    ("qkv_rows", _qkv_rows_shared_kv, [P.test_qkv_head_split_concat_and_one_hot]),
+]
+
+
+@pytest.mark.parametrize("name,fn,pins", MUTATIONS, ids=[f"{m[0]}-{m[1].__name__}" for m in MUTATIONS])
+def test_planted_mistake_is_caught(monkeypatch, name, fn, pins):
+    _patch(monkeypatch, name, fn)
+    for pin in pins:
+        with pytest.raises((AssertionError, ValueError, IndexError)):
+            pin()
