@@ -1,0 +1,351 @@
+"""Benchmark of one GPU's tensor-parallel shard path on MI355X.
+
+A step is one pass of the whole shard path of a Llama-70B-shaped layer at TP = 8
+and 4096 prefill tokens, every shard looped on this GPU:
+  for each shard r: QKV_r = X Wqkv_r^T + bqkv_r                 (column, head split)
+                    P_r   = Q_r Wo_r^T                          (row partial, A := Q)
+  Y1 = sum_r P_r + bo                                           (combine: sum)
+  for each shard r: H_r = silu(Y1 Wg_r^T + bg_r) * (Y1 Wu_r^T + bu_r)   (column pair)
+                    P_r = H_r Wd_r^T                            (row partial)
+  Y  = sum_r P_r + bd                                           (combine: sum)
+  QKV = concat_r QKV_r (Q | K | V segments), H = concat_r H_r   (combine: concat)
+Taking the shards (index arithmetic and copies) happens once at load, untimed.
+
+Prints one JSON line. Also measured in the same run: per-kernel times of the
+layer, the decode shards (M <= 64, weights rotated through > 1 GiB of copies so
+the 256 MB Infinity Cache cannot serve them), and the fp64 oracle on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--skip-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------------------
+# The layer
+# ----------------------------------------------------------------------------------------
+
+class Layer:
+    def __init__(self, shape):
+        import torch
+        import tensor_transformer_linear_col_amd as tp
+        import tp_inputs as I
+        self.tp, self.torch = tp, torch
+        BF = torch.bfloat16
+        s = shape
+        self.M = M = s.tokens[0]
+        self.h, self.inter, self.p = s.hidden, s.intermediate, s.tp
+        self.nh, self.nkv, self.d = s.n_heads, s.n_kv_heads, s.head_dim
+        p, h, inter = self.p, self.h, self.inter
+        self.nq = (self.nh // p + 2 * self.nkv // p) * self.d
+        self.ka = self.nh // p * self.d
+        self.i = inter // p
+        t0 = time.time()
+        aw = I.attn_weights(s, with_bias=True)
+        fw = I.ffn_weights(s, with_bias=True)
+        x = I.activations(M, h, I.activation_seed(s.seed, M))
+        log(f"inputs drawn in {time.time() - t0:.1f}s")
+        dev = lambda t: t.contiguous().cuda()
+        self.X = dev(x)
+        self.bo, self.bd = dev(aw["bo"]), dev(fw["bd"])
+        self.shards = []
+        full = {k: dev(v) for k, v in {**aw, **fw}.items()}
+        for r in range(p):
+            sh = {}
+            sh["Wqkv"] = torch.empty(self.nq, h, dtype=BF, device="cuda")
+            sh["bqkv"] = torch.empty(self.nq, dtype=BF, device="cuda")
+            tp.tp_shard_qkv(full["Wqkv"], h, self.nh, self.nkv, self.d, p, r, sh["Wqkv"])
+            tp.tp_shard_qkv(full["bqkv"], 1, self.nh, self.nkv, self.d, p, r, sh["bqkv"])
+            sh["Wo"] = torch.empty(h, self.ka, dtype=BF, device="cuda")
+            tp.tp_shard_weight(full["Wo"], h, self.nh * self.d, p, r, 1, sh["Wo"])
+            for nm in ("Wg", "Wu"):
+                sh[nm] = torch.empty(self.i, h, dtype=BF, device="cuda")
+                tp.tp_shard_weight(full[nm], inter, h, p, r, 0, sh[nm])
+            for nm in ("bg", "bu"):
+                sh[nm] = torch.empty(self.i, dtype=BF, device="cuda")
+                tp.tp_shard_weight(full[nm], inter, 1, p, r, 0, sh[nm])
+            sh["Wd"] = torch.empty(h, self.i, dtype=BF, device="cuda")
+            tp.tp_shard_weight(full["Wd"], h, inter, p, r, 1, sh["Wd"])
+            sh["QKV"] = torch.empty(M, self.nq, dtype=BF, device="cuda")
+            sh["Po"] = torch.empty(M, h, dtype=BF, device="cuda")
+            sh["H"] = torch.empty(M, self.i, dtype=BF, device="cuda")
+            sh["Pd"] = torch.empty(M, h, dtype=BF, device="cuda")
+            self.shards.append(sh)
+        del full
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        self.Y1 = torch.empty(M, h, dtype=BF, device="cuda")
+        self.Y = torch.empty(M, h, dtype=BF, device="cuda")
+        self.QKVc = torch.empty(M, (self.nh + 2 * self.nkv) * self.d, dtype=BF, device="cuda")
+        self.Hc = torch.empty(M, inter, dtype=BF, device="cuda")
+        self.seg = [self.nh // p * self.d, self.nkv // p * self.d, self.nkv // p * self.d]
+        # algorithmic work per step (2 M N K per product)
+        self.flops = {
+            "qkv": 2.0 * M * self.nq * h * p,
+            "o": 2.0 * M * h * self.ka * p,
+            "gateup": 2.0 * 2 * M * self.i * h * p,
+            "down": 2.0 * M * h * self.i * p,
+        }
+        self.total_flops = sum(self.flops.values())
+
+    def step(self, ev=None):
+        """One pass of the shard path. ev: optional dict name -> list of (start, end) events."""
+        tp, torch = self.tp, self.torch
+        M, h, p = self.M, self.h, self.p
+
+        def timed(name, fn):
+            if ev is None:
+                fn()
+                return
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            ev.setdefault(name, []).append((a, b))
+
+        for sh in self.shards:
+            timed("qkv", lambda: tp.tp_attn_proj_shard(self.X, sh["Wqkv"], sh["bqkv"], sh["QKV"], None, None, None,
+                                                      M, h, self.nh, self.nkv, self.d, p))
+            # A := Q: the shard's Q heads are the first ka columns of QKV_r (row stride nq)
+            timed("o", lambda: tp.tp_linear_row_partial(sh["QKV"], self.nq, sh["Wo"], sh["Po"], M,
+                                                        self.nh * self.d, h, p))
+        timed("sum", lambda: tp.tp_combine_sum([sh["Po"] for sh in self.shards], self.bo, self.Y1, M, h))
+        for sh in self.shards:
+            timed("gateup", lambda: tp.tp_mlp_shard(self.Y1, sh["Wg"], sh["Wu"], sh["bg"], sh["bu"], None,
+                                                    sh["H"], None, M, h, self.inter, p))
+            timed("down", lambda: tp.tp_linear_row_partial(sh["H"], self.i, sh["Wd"], sh["Pd"], M, self.inter,
+                                                           h, p))
+        timed("sum", lambda: tp.tp_combine_sum([sh["Pd"] for sh in self.shards], self.bd, self.Y, M, h))
+        timed("concat", lambda: tp.tp_combine_concat([sh["QKV"] for sh in self.shards], self.seg, self.QKVc, M))
+        timed("concat", lambda: tp.tp_combine_concat([sh["H"] for sh in self.shards], [self.i], self.Hc, M))
+
+
+def kernel_ms(ev):
+    out = {}
+    for name, pairs in ev.items():
+        ms = [a.elapsed_time(b) for a, b in pairs]
+        out[name] = sum(ms) / len(ms)
+    return out
+
+
+# ----------------------------------------------------------------------------------------
+# Decode shards (M <= 64): HBM-bound, weights rotated through > 1 GiB of copies
+# ----------------------------------------------------------------------------------------
+
+def hold_gpu(seconds):
+    import torch
+    try:
+        torch.cuda._sleep(int(seconds * 2.4e9))
+    except Exception:
+        pass
+
+
+def decode_bench(iters=30):
+    import torch
+    import tensor_transformer_linear_col_amd as tp
+    import tp_inputs as I
+    BF = torch.bfloat16
+    results = []
+    for shape in (I.LLAMA7B_FFN_TP2, I.LLAMA70B_FFN_TP4):
+        h, inter, p = shape.hidden, shape.intermediate, shape.tp
+        i = inter // p
+        wt = I.ffn_weights(shape, with_bias=False)
+        shard_bytes = 3 * i * h * 2
+        copies = max(1, -(-(1 << 30) // shard_bytes) + 1)
+        sets = []
+        base = [(wt["Wg"][r * i:(r + 1) * i].contiguous().cuda(), wt["Wu"][r * i:(r + 1) * i].contiguous().cuda(),
+                 wt["Wd"][:, r * i:(r + 1) * i].contiguous().cuda()) for r in range(p)]
+        for c in range(copies):
+            sets.append(base[c % p] if c < p else tuple(t.clone() for t in base[c % p]))
+        del wt
+        for M in shape.tokens:
+            x = I.activations(M, h, I.activation_seed(shape.seed, M)).cuda()
+            H = torch.empty(M, i, dtype=BF, device="cuda")
+            P = torch.empty(M, h, dtype=BF, device="cuda")
+            for c in range(len(sets)):  # warm
+                Wg, Wu, Wd = sets[c]
+                tp.tp_mlp_shard(x, Wg, Wu, None, None, None, H, None, M, h, inter, p)
+            torch.cuda.synchronize()
+            # Keep the GPU busy (a bounded spin) while the timed launches are queued, so the
+            # events time the kernels and not the host's launch rate.
+            hold_gpu(5e-3)
+            ev_g, ev_d = [], []
+            for it in range(iters):
+                Wg, Wu, Wd = sets[it % len(sets)]
+                a, b, c2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+                a.record()
+                tp.tp_mlp_shard(x, Wg, Wu, None, None, None, H, None, M, h, inter, p)
+                b.record()
+                tp.tp_linear_row_partial(H, i, Wd, P, M, inter, h, p)
+                c2.record()
+                ev_g.append((a, b))
+                ev_d.append((b, c2))
+            torch.cuda.synchronize()
+            gu = sorted(a.elapsed_time(b) for a, b in ev_g)[len(ev_g) // 2]
+            dn = sorted(a.elapsed_time(b) for a, b in ev_d)[len(ev_d) // 2]
+            gu_bytes = 2 * i * h * 2 + M * h * 2 + M * i * 2
+            dn_bytes = h * i * 2 + M * i * 2 + M * h * 2
+            for op, ms, by, fl in (("gateup_swiglu", gu, gu_bytes, 2.0 * 2 * M * i * h),
+                                   ("down_partial", dn, dn_bytes, 2.0 * M * h * i)):
+                gbs = by / (ms * 1e-3) / 1e9
+                results.append({"workload": shape.name, "M": M, "op": op, "us": round(ms * 1e3, 2),
+                                "GB_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 3),
+                                "TFLOP_s": round(fl / (ms * 1e-3) / 1e12, 2)})
+            log(f"decode {shape.name} M={M}: gate/up {gu*1e3:.1f} us, down {dn*1e3:.1f} us")
+        del sets, base
+        torch.cuda.empty_cache()
+    return results
+
+
+# ----------------------------------------------------------------------------------------
+# The fp64 oracle on the host, on a bounded sample of the same workload
+# ----------------------------------------------------------------------------------------
+
+def cpu_baseline(shape, target_s):
+    import numpy as np
+    import oracle as O
+    import tp_inputs as I
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    aw = I.attn_weights(shape, with_bias=True)
+    fw = I.ffn_weights(shape, with_bias=True)
+    w = {k: I.as_numpy_f64(v) for k, v in {**aw, **fw}.items()}
+    w.update(n_heads=shape.n_heads, n_kv_heads=shape.n_kv_heads, head_dim=shape.head_dim)
+    del aw, fw
+    M = shape.tokens[0]
+    x = I.as_numpy_f64(I.activations(M, shape.hidden, I.activation_seed(shape.seed, M)))
+    flop_per_token = 2.0 * shape.hidden * ((shape.n_heads + 2 * shape.n_kv_heads) * shape.head_dim
+                                           + shape.n_heads * shape.head_dim + 3 * shape.intermediate)
+    S = 16
+    while True:
+        t0 = time.perf_counter()
+        O.layer_unsharded(x[:S], w)
+        dt = time.perf_counter() - t0
+        if dt >= target_s * 0.5 or S >= M:
+            break
+        S = int(min(M, max(2 * S, S * target_s / max(dt, 1e-3))))
+    tflops = S * flop_per_token / dt / 1e12
+    return {"value": round(tflops, 4), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{S} of {M} tokens through the unsharded fp64 layer chain (numpy float64 BLAS), "
+                      f"{dt:.1f} s"}
+
+
+def traffic_for(kernel_src, name):
+    """HBM bytes per launch from stored rocprofv3 counter runs, if taken on this kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    if rec.get("kernel_source_sha256") != sha:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's shard path; --gpus {args.gpus} is not supported "
+              "(the cross-shard combine runs on one device here)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import tp_inputs as I
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    shape = I.LLAMA70B_LAYER_TP8
+    layer = Layer(shape)
+
+    for _ in range(args.warmup):
+        layer.step()
+    torch.cuda.synchronize()
+    ev = {}
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        layer.step(ev)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms_step = dt / args.steps * 1e3
+    per = kernel_ms(ev)  # ms per launch
+    tflops = layer.total_flops / (ms_step * 1e-3) / 1e12
+    log(f"layer step {ms_step:.3f} ms, {tflops:.1f} TFLOP/s; per launch (ms): "
+        + ", ".join(f"{k} {v:.4f}" for k, v in per.items()))
+
+    # dominant kernel: the fused gate/up + SwiGLU product (55% of the layer's flops)
+    gu_flops = layer.flops["gateup"] / layer.p
+    gu_ms = per["gateup"]
+    achieved = gu_flops / (gu_ms * 1e-3) / 1e12
+    traffic = traffic_for(os.path.join(ROOT, "tensor_transformer_linear_col_amd", "csrc", "k_gemm.hip"),
+                          "gemm_gateup_swiglu_llama70b_tp8_m4096")
+    kernels = {}
+    for name in ("qkv", "o", "gateup", "down"):
+        fl = layer.flops[name] / layer.p
+        kernels[name] = {"us_per_launch": round(per[name] * 1e3, 1),
+                         "TFLOP_s": round(fl / (per[name] * 1e-3) / 1e12, 1)}
+    M, h = layer.M, layer.h
+    sum_bytes = (layer.p + 1) * M * h * 2 + h * 2
+    kernels["combine_sum"] = {"us_per_launch": round(per["sum"] * 1e3, 1),
+                              "GB_s": round(sum_bytes / (per["sum"] * 1e-3) / 1e9, 1)}
+    kernels["combine_concat"] = {"us_per_launch": round(per["concat"] * 1e3, 1)}
+
+    decode = None if args.skip_decode else decode_bench()
+    cpu = None if args.skip_cpu_baseline else cpu_baseline(shape, args.cpu_seconds)
+
+    out = {
+        "metric": "TP-shard GEMM TFLOP/s + HBM GB/s (decode M=1..64, prefill M=4096), 1 GPU",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) bf16 weights and biases, N(0,1) activations)",
+        "config": {"workload": "llama70b-layer-prefill-tp8: all 8 shards of a 70B layer's QKV/O/gate/up/down "
+                               "products at 4096 tokens looped on one GPU, with on-device sum and concat combines",
+                   "tp_size": layer.p, "tokens": layer.M, "hidden": layer.h, "intermediate": layer.inter,
+                   "n_heads": layer.nh, "n_kv_heads": layer.nkv, "head_dim": layer.d,
+                   "flop_per_step": layer.total_flops},
+        "roofline": {"kernel": "gemm_kernel gate/up + SwiGLU (one shard, 4096 x 3584 x 8192, x2)",
+                     "bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": traffic},
+        "kernels": kernels,
+        "decode": decode,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,176 @@
+/*
+ * tp_linear.h -- one GPU's shard of a Megatron-style tensor-parallel layer on MI355X (gfx950).
+ *
+ * The operations follow these pages:
+ *   [P3] "Understanding Tensor Parallelism for Multi-GPU LLM Serving" (DevBytes):
+ *        section "How Tensor Parallelism Works Under the Hood" (Y = XW; column
+ *        parallelism splits W's output dimension, row parallelism its input
+ *        dimension and sums the partials) and the ColumnParallelLinear /
+ *        RowParallelLinear listing (per-partition sizes = size / world_size,
+ *        asserted divisible; the row layer's bias is added once after the sum).
+ *   [P4] "What is tensor parallelism?" (tecyfy), section "How a layer is split":
+ *        attention heads go to different GPUs; the TP size divides the heads.
+ *   [P5] "Tensor parallel serving" (Learn AI): the simulation script (column
+ *        shards are W[:split] / W[split:], combined by torch.cat on the last
+ *        axis), "Common mistakes" (row shards combine by summing), and the
+ *        researcher section (column then row: the intermediate is never
+ *        communicated).
+ *
+ * Conventions for every call:
+ *   - A weight is stored [out_features, in_features], row-major (the listing's
+ *     layout), so Y = X W of the pages is computed as Y = X * W^T (+ b).
+ *   - p = tp_size. Shard r owns the contiguous block [r*n/p, (r+1)*n/p) of the
+ *     split dimension.
+ *   - Every data pointer is a DEVICE pointer unless marked (host). The caller owns
+ *     every buffer; outputs must not alias inputs.
+ *   - Tensors are row-major and contiguous unless a leading dimension (ld*) is given.
+ *   - dtype TP_DTYPE_BF16: bf16 storage, fp32 accumulation, each output rounded
+ *     once to bf16 (round to nearest even). TP_DTYPE_F32: fp32 throughout.
+ *   - stream is a hipStream_t (NULL = the null stream). Each call validates its
+ *     arguments on the host, enqueues its kernels on `stream` and returns without
+ *     synchronising. On any validation error nothing is enqueued and no device
+ *     memory is touched.
+ *   - Alignment: every base pointer and every row stride in bytes must be a
+ *     multiple of 16 (TP_ERR_ALIGN otherwise). For bf16 this means K % 8 == 0,
+ *     for fp32 K % 4 == 0, for every row length that is read or written.
+ *   - Work space: kernels that split the reduction dimension across workgroups
+ *     keep fp32 partial sums in a device work space owned by the library, one per
+ *     (device, stream), allocated with hipMalloc on the first call that needs it
+ *     and grown when a larger one is needed. Calls on the same stream are
+ *     ordered by the stream; tp_release_workspaces() frees them all.
+ *   - Results are deterministic: every reduction runs in a fixed order.
+ *   - Errors are returned, never raised; TP_ERR_HIP reports a failed launch or
+ *     allocation (hipGetLastError after the launch).
+ */
+#ifndef TP_LINEAR_H
+#define TP_LINEAR_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TP_DTYPE_F32 = 0,
+    TP_DTYPE_BF16 = 1
+} tp_dtype_t;
+
+typedef enum {
+    TP_OK = 0,
+    TP_ERR_NULL = 1,        /* a required pointer is NULL */
+    TP_ERR_SHAPE = 2,       /* a size <= 0 (M may be 0: nothing is done), ld < width,
+                               tp_size outside [1, 64], rank outside [0, tp_size) */
+    TP_ERR_INDIVISIBLE = 3, /* a size that is split by tp_size is not divisible by it */
+    TP_ERR_DTYPE = 4,       /* unknown dtype, or an fp32 input with bf16 partials */
+    TP_ERR_ALIGN = 5,       /* a pointer or row stride is not a multiple of 16 bytes */
+    TP_ERR_HIP = 6          /* the HIP runtime reported an error */
+} tp_status_t;
+
+/* Column-parallel linear, shard r ([P3] "How ... Under the Hood", column parallelism;
+ * [P3] ColumnParallelLinear.forward; [P5] out_gpu0 = x @ W_gpu0.T + b_gpu0).
+ *   Y_r[M, out_features/p] = X[M, in_features] * W_r^T + b_r
+ *   X   : [M, in_features], the full input, replicated on every shard.
+ *   W_r : [out_features/p, in_features], the shard's contiguous block of output rows.
+ *   b_r : [out_features/p] or NULL (no bias).
+ *   Y_r : [M, out_features/p] output.
+ * TP_ERR_INDIVISIBLE if out_features % tp_size != 0 (the listing's assertion). */
+tp_status_t tp_linear_col(const void* X, const void* W_r, const void* b_r, void* Y_r,
+                          int64_t M, int64_t in_features, int64_t out_features,
+                          int32_t tp_size, tp_dtype_t dtype, void* stream);
+
+/* Row-parallel partial, shard r ([P3] row parallelism, RowParallelLinear.forward up to the
+ * all-reduce; the bias is NOT applied here -- see tp_combine_sum).
+ *   P_r[M, out_features] = X_r[M, in_features/p] * W_r^T
+ *   X_r : rows of in_features/p values with row stride ldx (elements, >= in_features/p).
+ *         Pass the previous column layer's local output with ldx = in_features/p, or
+ *         X + r*in_features/p with ldx = in_features to take the rank's slice of a full X
+ *         (the listing's x[..., r*k:(r+1)*k]).
+ *   W_r : [out_features, in_features/p], the shard's block of input columns, contiguous.
+ *   P_r : [M, out_features] partial, in partial_dtype (bf16 inputs allow bf16 or fp32
+ *         partials; fp32 inputs need fp32 partials).
+ * TP_ERR_INDIVISIBLE if in_features % tp_size != 0. */
+tp_status_t tp_linear_row_partial(const void* X_r, int64_t ldx, const void* W_r, void* P_r,
+                                  int64_t M, int64_t in_features, int64_t out_features,
+                                  int32_t tp_size, tp_dtype_t dtype, tp_dtype_t partial_dtype,
+                                  void* stream);
+
+/* Paired column -> row MLP shard with SwiGLU ([P3] FFN: column then row; [P5] researcher
+ * section "Column-parallel and row-parallel layers, paired": the intermediate stays local).
+ *   H_r[M, I/p] = silu(X * Wg_r^T + bg_r) * (X * Wu_r^T + bu_r),  silu(z) = z / (1 + e^-z)
+ *   P_r[M, hidden] = H_r * Wd_r^T   (partial, no bias; skipped when P_r is NULL)
+ *   X : [M, hidden]; Wg_r, Wu_r : [I/p, hidden]; bg_r, bu_r : [I/p] or NULL (both or neither);
+ *   Wd_r : [hidden, I/p] (may be NULL when P_r is NULL); H_r : [M, I/p] output (always
+ *   written: it is the row layer's input and the concat check's operand).
+ * TP_ERR_INDIVISIBLE if intermediate % tp_size != 0. */
+tp_status_t tp_mlp_shard(const void* X, const void* Wg_r, const void* Wu_r,
+                         const void* bg_r, const void* bu_r, const void* Wd_r,
+                         void* H_r, void* P_r, int64_t M, int64_t hidden, int64_t intermediate,
+                         int32_t tp_size, tp_dtype_t dtype, tp_dtype_t partial_dtype,
+                         void* stream);
+
+/* Head-split attention projections, shard r ([P4] "How a layer is split": heads go to
+ * different GPUs and the TP size divides the heads; [P5] one sum per attention block).
+ *   QKV_r[M, (Hq/p + 2*G/p)*d] = X * Wqkv_r^T + bqkv_r   (skipped when QKV_r is NULL)
+ *       Wqkv_r rows are [Q heads r*Hq/p .. | K heads r*G/p .. | V heads r*G/p ..], each head
+ *       head_dim rows, i.e. the output segments are (Hq/p*d, G/p*d, G/p*d).
+ *   P_r[M, hidden] = A_r * Wo_r^T   (partial, no bias; skipped when P_r is NULL)
+ *       A_r : [M, Hq/p*d], the shard's attention output (its own heads).
+ *       Wo_r : [hidden, Hq/p*d], the O projection's input-column block of those heads.
+ *   Hq = n_heads, G = n_kv_heads, d = head_dim; bqkv_r may be NULL.
+ * TP_ERR_INDIVISIBLE if n_heads % tp_size or n_kv_heads % tp_size != 0. */
+tp_status_t tp_attn_proj_shard(const void* X, const void* Wqkv_r, const void* bqkv_r, void* QKV_r,
+                               const void* A_r, const void* Wo_r, void* P_r,
+                               int64_t M, int64_t hidden, int32_t n_heads, int32_t n_kv_heads,
+                               int32_t head_dim, int32_t tp_size, tp_dtype_t dtype,
+                               tp_dtype_t partial_dtype, void* stream);
+
+/* Concat of column-parallel outputs, on one device ([P5] torch.cat([...], dim=-1) and its
+ * walkthrough). shards (host array of tp_size device pointers) each hold [M, S] with
+ * S = sum(seg_widths) (host array of nseg widths). Segment j of shard r goes to output
+ * columns p*(w_0+..+w_{j-1}) + r*w_j .. +w_j, so nseg = 1 is a plain concat in rank order
+ * and seg_widths = (Hq/p*d, G/p*d, G/p*d) rebuilds the unsharded [Q | K | V].
+ *   Y : [M, p*S]. Pure copy, exact. */
+tp_status_t tp_combine_concat(const void* const* shards, int32_t tp_size,
+                              const int64_t* seg_widths, int32_t nseg, void* Y, int64_t M,
+                              tp_dtype_t dtype, void* stream);
+
+/* Sum of row-parallel partials plus the bias, once ([P3] all_reduce(SUM) then + bias;
+ * [P5] "Common mistakes": summing, not concatenating). Computed on one device by reading
+ * every shard's partial: Y = sum_{r=0}^{p-1} P_r + b, fp32 accumulation with ranks in
+ * ascending order and one rounding to out_dtype.
+ *   partials : host array of tp_size device pointers, each [M, N] in partial_dtype.
+ *   b : [N] in out_dtype, or NULL.  Y : [M, N] in out_dtype. */
+tp_status_t tp_combine_sum(const void* const* partials, int32_t tp_size, tp_dtype_t partial_dtype,
+                           const void* b, void* Y, int64_t M, int64_t N, tp_dtype_t out_dtype,
+                           void* stream);
+
+/* Take shard `rank` of an unsharded weight into a contiguous buffer ([P3] listing: each GPU
+ * stores only its shard; [P5] W[:split], W[split:]).
+ *   axis 0 (column-parallel): W_r = W[r*out/p:(r+1)*out/p, :] -> [out/p, in]
+ *   axis 1 (row-parallel):    W_r = W[:, r*in/p:(r+1)*in/p]   -> [out, in/p]
+ *   A bias is sharded with axis 0 and in_features = 1 (no 16-byte row rule then).
+ * TP_ERR_INDIVISIBLE if the split size is not divisible by tp_size; TP_ERR_SHAPE for a bad
+ * axis or rank. Exact copy. */
+tp_status_t tp_shard_weight(const void* W, int64_t out_features, int64_t in_features,
+                            int32_t tp_size, int32_t rank, int32_t axis, void* W_r,
+                            tp_dtype_t dtype, void* stream);
+
+/* Take shard `rank` of a fused [Wq; Wk; Wv] weight ([(Hq + 2G)*d, in_features]) or, with
+ * in_features = 1, of its bias: the rows of Q heads r*Hq/p.., K heads r*G/p.., V heads
+ * r*G/p.., in that order -> [(Hq/p + 2G/p)*d, in_features]. */
+tp_status_t tp_shard_qkv(const void* Wqkv, int64_t in_features, int32_t n_heads, int32_t n_kv_heads,
+                         int32_t head_dim, int32_t tp_size, int32_t rank, void* Wqkv_r,
+                         tp_dtype_t dtype, void* stream);
+
+/* Frees every work space the library holds. No call may be in flight on any stream. */
+tp_status_t tp_release_workspaces(void);
+
+/* Static, human-readable name of a status code. */
+const char* tp_status_string(tp_status_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TP_LINEAR_H */

@@ -1,0 +1,287 @@
+// C ABI of the tensor-parallel shard library: host-side validation, then kernel
+// launches on the caller's stream. See include/tp_linear.h for the contract.
+#include <algorithm>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "tp_internal.h"
+
+using namespace tp;
+
+namespace {
+
+constexpr int32_t kMaxTP = 64;
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+
+bool dtype_ok(tp_dtype_t d) { return d == TP_DTYPE_F32 || d == TP_DTYPE_BF16; }
+size_t elem_size(tp_dtype_t d) { return d == TP_DTYPE_F32 ? 4 : 2; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// bf16 operands are read with 16-byte loads: base and row stride must allow it.
+tp_status_t check_vec_operand(const void* p, int64_t ld_elems, tp_dtype_t dt) {
+    if (dt != TP_DTYPE_BF16) return TP_OK;
+    if (!aligned16(p) || (ld_elems * 2) % 16 != 0) return TP_ERR_ALIGN;
+    return TP_OK;
+}
+
+tp_status_t check_dims(int64_t M, std::initializer_list<int64_t> pos) {
+    if (M < 0 || M > kMaxDim) return TP_ERR_SHAPE;
+    for (int64_t v : pos)
+        if (v <= 0 || v > kMaxDim) return TP_ERR_SHAPE;
+    return TP_OK;
+}
+
+#define TP_TRY(expr)                       \
+    do {                                   \
+        const tp_status_t st_ = (expr);    \
+        if (st_ != TP_OK) return st_;      \
+    } while (0)
+
+tp_status_t launch_linear(const LinearDesc& d, hipStream_t s) {
+    if (d.M == 0) return TP_OK;
+    if (d.in_dtype == TP_DTYPE_F32) return launch_f32(d, s);
+    if (d.M <= 64) return launch_skinny(d, s);
+    return launch_gemm(d, s);
+}
+
+// ---- work space cache: one per (device, stream) --------------------------------------
+struct WsEntry {
+    void* base = nullptr;
+    size_t partial_floats = 0;
+    size_t counters = 0;
+};
+
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, WsEntry> g_ws;
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+}  // namespace
+
+namespace tp {
+
+tp_status_t get_workspace(hipStream_t stream, size_t partial_floats, size_t n_counters, Workspace* out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return TP_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    WsEntry& e = g_ws[{dev, stream}];
+    if (e.base == nullptr || e.partial_floats < partial_floats || e.counters < n_counters) {
+        const size_t want_f = std::max(e.partial_floats, round_up(partial_floats, 1 << 16));
+        const size_t want_c = std::max(e.counters, round_up(n_counters, 1 << 12));
+        if (e.base) {
+            // Work still queued on this stream may use the old buffer.
+            if (hipStreamSynchronize(stream) != hipSuccess) return TP_ERR_HIP;
+            if (hipFree(e.base) != hipSuccess) return TP_ERR_HIP;
+            e.base = nullptr;
+        }
+        void* p = nullptr;
+        if (hipMalloc(&p, want_c * sizeof(unsigned) + want_f * sizeof(float)) != hipSuccess) return TP_ERR_HIP;
+        e.base = p;
+        e.partial_floats = want_f;
+        e.counters = want_c;
+        // Counters start at zero; every split-K tile resets its own counter when done.
+        TP_TRY(launch_fill_u32(static_cast<unsigned*>(p), want_c, 0u, stream));
+    }
+    out->counters = static_cast<unsigned*>(e.base);
+    out->partials = reinterpret_cast<float*>(static_cast<unsigned*>(e.base) + e.counters);
+    return TP_OK;
+}
+
+}  // namespace tp
+
+extern "C" {
+
+const char* tp_status_string(tp_status_t s) {
+    switch (s) {
+        case TP_OK: return "TP_OK";
+        case TP_ERR_NULL: return "TP_ERR_NULL: a required pointer is NULL";
+        case TP_ERR_SHAPE: return "TP_ERR_SHAPE: invalid size, stride, tp_size or rank";
+        case TP_ERR_INDIVISIBLE: return "TP_ERR_INDIVISIBLE: a split size is not divisible by tp_size";
+        case TP_ERR_DTYPE: return "TP_ERR_DTYPE: unsupported dtype combination";
+        case TP_ERR_ALIGN: return "TP_ERR_ALIGN: a bf16 operand or its row stride is not 16-byte aligned";
+        case TP_ERR_HIP: return "TP_ERR_HIP: the HIP runtime reported an error";
+    }
+    return "unknown tp_status_t";
+}
+
+tp_status_t tp_linear_col(const void* X, const void* W_r, const void* b_r, void* Y_r, int64_t M,
+                          int64_t in_features, int64_t out_features, int32_t tp_size, tp_dtype_t dtype,
+                          void* stream) {
+    if (!X || !W_r || !Y_r) return TP_ERR_NULL;
+    if (!dtype_ok(dtype)) return TP_ERR_DTYPE;
+    TP_TRY(check_dims(M, {in_features, out_features}));
+    if (tp_size < 1 || tp_size > kMaxTP) return TP_ERR_SHAPE;
+    if (out_features % tp_size != 0) return TP_ERR_INDIVISIBLE;
+    const int64_t n = out_features / tp_size;
+    TP_TRY(check_vec_operand(X, in_features, dtype));
+    TP_TRY(check_vec_operand(W_r, in_features, dtype));
+    LinearDesc d{X, in_features, W_r, nullptr, b_r, nullptr, Y_r, n, M, n, in_features, dtype, dtype, false};
+    return launch_linear(d, static_cast<hipStream_t>(stream));
+}
+
+tp_status_t tp_linear_row_partial(const void* X_r, int64_t ldx, const void* W_r, void* P_r, int64_t M,
+                                  int64_t in_features, int64_t out_features, int32_t tp_size, tp_dtype_t dtype,
+                                  tp_dtype_t partial_dtype, void* stream) {
+    if (!X_r || !W_r || !P_r) return TP_ERR_NULL;
+    if (!dtype_ok(dtype) || !dtype_ok(partial_dtype)) return TP_ERR_DTYPE;
+    if (dtype == TP_DTYPE_F32 && partial_dtype != TP_DTYPE_F32) return TP_ERR_DTYPE;
+    TP_TRY(check_dims(M, {in_features, out_features}));
+    if (tp_size < 1 || tp_size > kMaxTP) return TP_ERR_SHAPE;
+    if (in_features % tp_size != 0) return TP_ERR_INDIVISIBLE;
+    const int64_t k = in_features / tp_size;
+    if (ldx < k) return TP_ERR_SHAPE;
+    TP_TRY(check_vec_operand(X_r, ldx, dtype));
+    TP_TRY(check_vec_operand(W_r, k, dtype));
+    LinearDesc d{X_r, ldx, W_r, nullptr, nullptr, nullptr, P_r, out_features, M, out_features, k, dtype,
+                 partial_dtype, false};
+    return launch_linear(d, static_cast<hipStream_t>(stream));
+}
+
+tp_status_t tp_mlp_shard(const void* X, const void* Wg_r, const void* Wu_r, const void* bg_r, const void* bu_r,
+                         const void* Wd_r, void* H_r, void* P_r, int64_t M, int64_t hidden, int64_t intermediate,
+                         int32_t tp_size, tp_dtype_t dtype, tp_dtype_t partial_dtype, void* stream) {
+    if (!X || !Wg_r || !Wu_r || !H_r) return TP_ERR_NULL;
+    if (P_r && !Wd_r) return TP_ERR_NULL;
+    if ((bg_r == nullptr) != (bu_r == nullptr)) return TP_ERR_NULL;
+    if (!dtype_ok(dtype) || !dtype_ok(partial_dtype)) return TP_ERR_DTYPE;
+    if (dtype == TP_DTYPE_F32 && partial_dtype != TP_DTYPE_F32) return TP_ERR_DTYPE;
+    TP_TRY(check_dims(M, {hidden, intermediate}));
+    if (tp_size < 1 || tp_size > kMaxTP) return TP_ERR_SHAPE;
+    if (intermediate % tp_size != 0) return TP_ERR_INDIVISIBLE;
+    const int64_t i = intermediate / tp_size;
+    TP_TRY(check_vec_operand(X, hidden, dtype));
+    TP_TRY(check_vec_operand(Wg_r, hidden, dtype));
+    TP_TRY(check_vec_operand(Wu_r, hidden, dtype));
+    if (P_r) {
+        TP_TRY(check_vec_operand(H_r, i, dtype));
+        TP_TRY(check_vec_operand(Wd_r, i, dtype));
+    }
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    LinearDesc up{X, hidden, Wg_r, Wu_r, bg_r, bu_r, H_r, i, M, i, hidden, dtype, dtype, true};
+    TP_TRY(launch_linear(up, s));
+    if (!P_r) return TP_OK;
+    LinearDesc down{H_r, i, Wd_r, nullptr, nullptr, nullptr, P_r, hidden, M, hidden, i, dtype, partial_dtype, false};
+    return launch_linear(down, s);
+}
+
+tp_status_t tp_attn_proj_shard(const void* X, const void* Wqkv_r, const void* bqkv_r, void* QKV_r, const void* A_r,
+                               const void* Wo_r, void* P_r, int64_t M, int64_t hidden, int32_t n_heads,
+                               int32_t n_kv_heads, int32_t head_dim, int32_t tp_size, tp_dtype_t dtype,
+                               tp_dtype_t partial_dtype, void* stream) {
+    if (QKV_r && (!X || !Wqkv_r)) return TP_ERR_NULL;
+    if (P_r && (!A_r || !Wo_r)) return TP_ERR_NULL;
+    if (!dtype_ok(dtype) || !dtype_ok(partial_dtype)) return TP_ERR_DTYPE;
+    if (dtype == TP_DTYPE_F32 && partial_dtype != TP_DTYPE_F32) return TP_ERR_DTYPE;
+    TP_TRY(check_dims(M, {hidden, n_heads, n_kv_heads, head_dim}));
+    if (tp_size < 1 || tp_size > kMaxTP) return TP_ERR_SHAPE;
+    if (n_heads % tp_size != 0 || n_kv_heads % tp_size != 0) return TP_ERR_INDIVISIBLE;
+    const int64_t hq = n_heads / tp_size, hk = n_kv_heads / tp_size;
+    const int64_t nqkv = (hq + 2 * hk) * head_dim;
+    const int64_t ka = hq * head_dim;
+    if (nqkv > kMaxDim) return TP_ERR_SHAPE;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (QKV_r) {
+        TP_TRY(check_vec_operand(X, hidden, dtype));
+        TP_TRY(check_vec_operand(Wqkv_r, hidden, dtype));
+    }
+    if (P_r) {
+        TP_TRY(check_vec_operand(A_r, ka, dtype));
+        TP_TRY(check_vec_operand(Wo_r, ka, dtype));
+    }
+    if (QKV_r) {
+        LinearDesc q{X, hidden, Wqkv_r, nullptr, bqkv_r, nullptr, QKV_r, nqkv, M, nqkv, hidden, dtype, dtype, false};
+        TP_TRY(launch_linear(q, s));
+    }
+    if (P_r) {
+        LinearDesc o{A_r, ka, Wo_r, nullptr, nullptr, nullptr, P_r, hidden, M, hidden, ka, dtype, partial_dtype, false};
+        TP_TRY(launch_linear(o, s));
+    }
+    return TP_OK;
+}
+
+tp_status_t tp_combine_concat(const void* const* shards, int32_t tp_size, const int64_t* seg_widths, int32_t nseg,
+                              void* Y, int64_t M, tp_dtype_t dtype, void* stream) {
+    if (!shards || !seg_widths || !Y) return TP_ERR_NULL;
+    if (!dtype_ok(dtype)) return TP_ERR_DTYPE;
+    if (tp_size < 1 || tp_size > kMaxTP || nseg < 1 || nseg > 8 || M < 0 || M > kMaxDim) return TP_ERR_SHAPE;
+    for (int32_t r = 0; r < tp_size; ++r)
+        if (!shards[r]) return TP_ERR_NULL;
+    for (int32_t j = 0; j < nseg; ++j)
+        if (seg_widths[j] <= 0 || seg_widths[j] > kMaxDim) return TP_ERR_SHAPE;
+    return launch_concat(shards, tp_size, seg_widths, nseg, Y, M, elem_size(dtype), static_cast<hipStream_t>(stream));
+}
+
+tp_status_t tp_combine_sum(const void* const* partials, int32_t tp_size, tp_dtype_t partial_dtype, const void* b,
+                           void* Y, int64_t M, int64_t N, tp_dtype_t out_dtype, void* stream) {
+    if (!partials || !Y) return TP_ERR_NULL;
+    if (!dtype_ok(partial_dtype) || !dtype_ok(out_dtype)) return TP_ERR_DTYPE;
+    TP_TRY(check_dims(M, {N}));
+    if (tp_size < 1 || tp_size > kMaxTP) return TP_ERR_SHAPE;
+    for (int32_t r = 0; r < tp_size; ++r)
+        if (!partials[r]) return TP_ERR_NULL;
+    return launch_combine_sum(partials, tp_size, partial_dtype, b, Y, M, N, out_dtype,
+                              static_cast<hipStream_t>(stream));
+}
+
+tp_status_t tp_shard_weight(const void* W, int64_t out_features, int64_t in_features, int32_t tp_size, int32_t rank,
+                            int32_t axis, void* W_r, tp_dtype_t dtype, void* stream) {
+    if (!W || !W_r) return TP_ERR_NULL;
+    if (!dtype_ok(dtype)) return TP_ERR_DTYPE;
+    TP_TRY(check_dims(0, {out_features, in_features}));
+    if (tp_size < 1 || tp_size > kMaxTP || rank < 0 || rank >= tp_size || (axis != 0 && axis != 1))
+        return TP_ERR_SHAPE;
+    const size_t es = elem_size(dtype);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (axis == 0) {
+        if (out_features % tp_size != 0) return TP_ERR_INDIVISIBLE;
+        const int64_t rows = out_features / tp_size;
+        const char* src = static_cast<const char*>(W) + (size_t)(rank * rows) * in_features * es;
+        return launch_copy2d(src, in_features, W_r, in_features, rows, in_features, es, s);
+    }
+    if (in_features % tp_size != 0) return TP_ERR_INDIVISIBLE;
+    const int64_t cols = in_features / tp_size;
+    const char* src = static_cast<const char*>(W) + (size_t)(rank * cols) * es;
+    return launch_copy2d(src, in_features, W_r, cols, out_features, cols, es, s);
+}
+
+tp_status_t tp_shard_qkv(const void* Wqkv, int64_t in_features, int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
+                         int32_t tp_size, int32_t rank, void* Wqkv_r, tp_dtype_t dtype, void* stream) {
+    if (!Wqkv || !Wqkv_r) return TP_ERR_NULL;
+    if (!dtype_ok(dtype)) return TP_ERR_DTYPE;
+    TP_TRY(check_dims(0, {in_features, n_heads, n_kv_heads, head_dim}));
+    if (tp_size < 1 || tp_size > kMaxTP || rank < 0 || rank >= tp_size) return TP_ERR_SHAPE;
+    if (n_heads % tp_size != 0 || n_kv_heads % tp_size != 0) return TP_ERR_INDIVISIBLE;
+    const size_t es = elem_size(dtype);
+    const int64_t d = head_dim, hq = n_heads / tp_size, hk = n_kv_heads / tp_size;
+    const int64_t src_rows[3] = {rank * hq * d, n_heads * d + rank * hk * d, (n_heads + n_kv_heads) * d + rank * hk * d};
+    const int64_t nrows[3] = {hq * d, hk * d, hk * d};
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    int64_t dst_row = 0;
+    for (int j = 0; j < 3; ++j) {
+        const char* src = static_cast<const char*>(Wqkv) + (size_t)src_rows[j] * in_features * es;
+        char* dst = static_cast<char*>(Wqkv_r) + (size_t)dst_row * in_features * es;
+        TP_TRY(launch_copy2d(src, in_features, dst, in_features, nrows[j], in_features, es, s));
+        dst_row += nrows[j];
+    }
+    return TP_OK;
+}
+
+tp_status_t tp_release_workspaces(void) {
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    tp_status_t st = TP_OK;
+    for (auto& kv : g_ws) {
+        if (kv.second.base) {
+            int prev = 0;
+            hipGetDevice(&prev);
+            hipSetDevice(kv.first.first);
+            if (hipStreamSynchronize(kv.first.second) != hipSuccess || hipFree(kv.second.base) != hipSuccess)
+                st = TP_ERR_HIP;
+            hipSetDevice(prev);
+        }
+    }
+    g_ws.clear();
+    return st;
+}
+
+}  // extern "C"

@@ -1,0 +1,152 @@
+"""The C ABI on the CPU: the library loads, exports every declared function, and
+rejects bad arguments on the host before any HIP call (fake, never-dereferenced
+pointers are enough for that). No call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tensor_transformer_linear_col_amd as tp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tp_linear.h")
+
+OK, NULL, SHAPE, INDIV, DTYPE, ALIGN, HIP = range(7)
+F32, BF16 = 0, 1
+P = 0x100000  # a 16-byte aligned fake device address, never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:tp_status_t|const char\*)\s+(tp_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(tp.lib_path()):
+        pytest.skip("libtp.so not built")
+    return tp.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) == 10, names
+    for name in names:
+        assert hasattr(L, name), name
+    assert set(names) == set(tp.EXPORTS)
+
+
+def test_status_strings(L):
+    for code in range(7):
+        assert tp.tp_status_string(code).startswith(
+            ["TP_OK", "TP_ERR_NULL", "TP_ERR_SHAPE", "TP_ERR_INDIVISIBLE", "TP_ERR_DTYPE",
+             "TP_ERR_ALIGN", "TP_ERR_HIP"][code])
+    assert "unknown" in tp.tp_status_string(99)
+
+
+def col(L, X=P, W=P, b=0, Y=P, M=4, K=4096, N=11008, p=2, dt=BF16):
+    return L.tp_linear_col(X, W, b, Y, M, K, N, p, dt, None)
+
+
+def test_linear_col_errors(L):
+    assert col(L, X=0) == NULL
+    assert col(L, W=0) == NULL
+    assert col(L, Y=0) == NULL
+    assert col(L, N=11008, p=3) == INDIV           # the listing's out_features % world_size assert
+    assert col(L, p=0) == SHAPE
+    assert col(L, p=65) == SHAPE
+    assert col(L, M=-1) == SHAPE
+    assert col(L, K=0) == SHAPE
+    assert col(L, N=0) == SHAPE
+    assert col(L, dt=7) == DTYPE
+    assert col(L, X=P + 8) == ALIGN                # bf16 operand read with 16-byte loads
+    assert col(L, K=4100) == ALIGN                 # row stride 8200 B is not a multiple of 16
+    assert col(L, M=0) == OK                       # nothing to do: returns before any HIP call
+    # fp32 has no alignment rule (the toy's 3-wide shards)
+    assert col(L, X=P + 4, K=8, N=6, p=2, dt=F32, M=0) == OK
+
+
+def row(L, X=P, ldx=None, W=P, Y=P, M=4, K=11008, N=4096, p=2, dt=BF16, pdt=BF16):
+    ldx = K // p if ldx is None else ldx
+    return L.tp_linear_row_partial(X, ldx, W, Y, M, K, N, p, dt, pdt, None)
+
+
+def test_linear_row_partial_errors(L):
+    assert row(L, X=0) == NULL
+    assert row(L, K=11008, p=3, ldx=4000) == INDIV   # in_features % world_size
+    assert row(L, ldx=5503) == SHAPE                 # ldx < in_features / p
+    assert row(L, dt=F32, pdt=BF16) == DTYPE         # fp32 inputs need fp32 partials
+    assert row(L, pdt=3) == DTYPE
+    assert row(L, ldx=5505) == ALIGN
+    assert row(L, M=0) == OK
+    assert row(L, M=0, pdt=F32) == OK                # bf16 inputs may keep fp32 partials
+
+
+def mlp(L, X=P, Wg=P, Wu=P, bg=0, bu=0, Wd=P, H=P, Pr=P, M=1, h=4096, i=11008, p=2, dt=BF16, pdt=BF16):
+    return L.tp_mlp_shard(X, Wg, Wu, bg, bu, Wd, H, Pr, M, h, i, p, dt, pdt, None)
+
+
+def test_mlp_shard_errors(L):
+    assert mlp(L, H=0) == NULL
+    assert mlp(L, Wd=0) == NULL
+    assert mlp(L, bg=P) == NULL                      # gate and up biases come together
+    assert mlp(L, i=11008, p=3) == INDIV
+    assert mlp(L, i=28672, p=5) == INDIV
+    assert mlp(L, Wg=P + 2) == ALIGN
+    assert mlp(L, dt=F32, pdt=BF16) == DTYPE
+    assert mlp(L, M=0) == OK
+    assert mlp(L, M=0, Wd=0, Pr=0) == OK             # down projection skipped
+
+
+def attn(L, X=P, Wqkv=P, b=0, QKV=P, A=P, Wo=P, Pr=P, M=1, h=8192, nh=64, nkv=8, d=128, p=8,
+         dt=BF16, pdt=BF16):
+    return L.tp_attn_proj_shard(X, Wqkv, b, QKV, A, Wo, Pr, M, h, nh, nkv, d, p, dt, pdt, None)
+
+
+def test_attn_proj_shard_errors(L):
+    assert attn(L, p=3) == INDIV                     # TP size must divide the heads
+    assert attn(L, nkv=8, p=16) == INDIV             # ... the KV heads too
+    assert attn(L, A=0) == NULL
+    assert attn(L, QKV=0, X=0, Wqkv=0, M=0) == OK    # QKV half skipped
+    assert attn(L, Pr=0, A=0, Wo=0, M=0) == OK       # O half skipped
+    assert attn(L, d=0) == SHAPE
+    assert attn(L, M=0) == OK
+
+
+def test_combine_errors(L):
+    ptrs = (ctypes.c_void_p * 2)(P, P)
+    bad = (ctypes.c_void_p * 2)(P, 0)
+    segs = (ctypes.c_int64 * 3)(1024, 128, 128)
+    assert L.tp_combine_concat(None, 2, segs, 3, P, 4, BF16, None) == NULL
+    assert L.tp_combine_concat(bad, 2, segs, 3, P, 4, BF16, None) == NULL
+    assert L.tp_combine_concat(ptrs, 2, segs, 0, P, 4, BF16, None) == SHAPE
+    assert L.tp_combine_concat(ptrs, 2, segs, 9, P, 4, BF16, None) == SHAPE
+    assert L.tp_combine_concat(ptrs, 0, segs, 3, P, 4, BF16, None) == SHAPE
+    assert L.tp_combine_concat(ptrs, 2, segs, 3, P, 4, 5, None) == DTYPE
+    zero = (ctypes.c_int64 * 1)(0)
+    assert L.tp_combine_concat(ptrs, 2, zero, 1, P, 4, BF16, None) == SHAPE
+    assert L.tp_combine_sum(None, 2, BF16, 0, P, 4, 4096, BF16, None) == NULL
+    assert L.tp_combine_sum(bad, 2, BF16, 0, P, 4, 4096, BF16, None) == NULL
+    assert L.tp_combine_sum(ptrs, 2, BF16, 0, 0, 4, 4096, BF16, None) == NULL
+    assert L.tp_combine_sum(ptrs, 2, BF16, 0, P, 4, 0, BF16, None) == SHAPE
+    assert L.tp_combine_sum(ptrs, 2, 9, 0, P, 4, 4096, BF16, None) == DTYPE
+    assert L.tp_combine_sum(ptrs, 99, BF16, 0, P, 4, 4096, BF16, None) == SHAPE
+
+
+def test_shard_errors(L):
+    assert L.tp_shard_weight(0, 6, 8, 2, 0, 0, P, F32, None) == NULL
+    assert L.tp_shard_weight(P, 6, 8, 2, 2, 0, P, F32, None) == SHAPE   # rank >= p
+    assert L.tp_shard_weight(P, 6, 8, 2, -1, 0, P, F32, None) == SHAPE
+    assert L.tp_shard_weight(P, 6, 8, 2, 0, 2, P, F32, None) == SHAPE   # axis
+    assert L.tp_shard_weight(P, 9, 8, 2, 0, 0, P, F32, None) == INDIV   # 9 outputs over 2 shards
+    assert L.tp_shard_weight(P, 6, 9, 2, 0, 1, P, F32, None) == INDIV
+    assert L.tp_shard_qkv(P, 8192, 64, 8, 128, 3, 0, P, BF16, None) == INDIV
+    assert L.tp_shard_qkv(P, 8192, 64, 8, 128, 8, 8, P, BF16, None) == SHAPE
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(1, 8)
+    with pytest.raises(ValueError):
+        tp.tp_linear_col(x, x, None, x, 1, 8, 6, 2)

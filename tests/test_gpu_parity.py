@@ -1,0 +1,326 @@
+"""GPU parity of every entry point against the fp64 oracle, at sizes the oracle finishes
+in seconds that still span several tiles, ragged tails and the degenerate cases.
+Every call goes through the C ABI (the ctypes binding)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import tensor_transformer_linear_col_amd as tp
+import tp_inputs as I
+from conftest import read_golden
+from gpu_util import (BF16_TOL, F32_TOL, canaries_intact, canary_buffer, dev, err, host64,
+                      log_case)
+
+pytestmark = pytest.mark.gpu
+
+
+# ---- the toy layer: fp32, TP = 2 ("Tensor parallel serving", simulation script) ------------
+
+def test_toy_column_split_concat_fp32():
+    log_case("toy column split fp32")
+    x, w, b = I.toy_layer()
+    X, W, B = dev(x), dev(w), dev(b)
+    shards = []
+    for r in range(2):
+        W_r = torch.empty(3, 8, device="cuda")
+        b_r = torch.empty(3, device="cuda")
+        tp.tp_shard_weight(W, 6, 8, 2, r, 0, W_r)
+        tp.tp_shard_weight(B, 6, 1, 2, r, 0, b_r)
+        Y_r = torch.empty(1, 3, device="cuda")
+        tp.tp_linear_col(X, W_r, b_r, Y_r, 1, 8, 6, 2)
+        shards.append(Y_r)
+    Y = torch.empty(1, 6, device="cuda")
+    tp.tp_combine_concat(shards, [3], Y, 1)
+    torch.cuda.synchronize()
+    ref = O.linear(host64(x), host64(w), host64(b))
+    assert err(Y, ref) <= F32_TOL
+    printed = [float(v) for v in read_golden("toy_tp2.txt")["combined_output_round4"]]
+    np.testing.assert_array_equal(np.round(host64(Y)[0], 4), printed)
+    assert W_r.numel() == 24   # "GPU 0 held 24 of 48 weight values"
+
+
+def test_toy_row_split_sum_fp32():
+    log_case("toy row split fp32")
+    x, w, b = I.toy_layer()
+    X, W, B = dev(x), dev(w), dev(b)
+    parts = []
+    for r in range(2):
+        W_r = torch.empty(6, 4, device="cuda")
+        tp.tp_shard_weight(W, 6, 8, 2, r, 1, W_r)
+        P_r = torch.empty(1, 6, device="cuda")
+        tp.tp_linear_row_partial(X[:, r * 4:], 8, W_r, P_r, 1, 8, 6, 2)   # the rank's slice of x
+        parts.append(P_r)
+    Y = torch.empty(1, 6, device="cuda")
+    tp.tp_combine_sum(parts, B, Y, 1, 6)
+    torch.cuda.synchronize()
+    ref = O.linear(host64(x), host64(w), host64(b))
+    assert err(Y, ref) <= F32_TOL
+    printed = [float(v) for v in read_golden("toy_tp2.txt")["full_output_round4"]]
+    np.testing.assert_array_equal(np.round(host64(Y)[0], 4), printed)
+
+
+# ---- bf16 column linear: decode kernel (M <= 64) and prefill kernel (M > 64) -----------------
+
+SHAPES = [  # (M, K, N): ragged M, K and N tails, several tiles, both kernels
+    (1, 8, 16), (1, 40, 3), (1, 4096, 1280), (2, 1000, 200), (5, 520, 24), (8, 4096, 344),
+    (16, 264, 48), (17, 1032, 100), (33, 2048, 130), (48, 96, 64), (64, 4104, 200), (65, 512, 96),
+    (100, 1000, 300), (130, 264, 257), (256, 1024, 512), (300, 2056, 520), (513, 640, 264),
+]
+
+
+@pytest.mark.parametrize("bias", [False, True])
+@pytest.mark.parametrize("M,K,N", SHAPES)
+def test_linear_col_bf16(M, K, N, bias):
+    log_case("linear_col bf16", M, K, N, bias)
+    seed = M * 7 + K * 3 + N
+    x = I.activations(M, K, seed)
+    w = I.weight(N, K, seed + 1)
+    b = I.bias(N, seed + 2) if bias else None
+    buf, Y = canary_buffer((M, N), torch.bfloat16)
+    tp.tp_linear_col(dev(x), dev(w), dev(b), Y, M, K, N, 1)
+    torch.cuda.synchronize()
+    ref = O.linear(host64(x), host64(w), None if b is None else host64(b))
+    assert err(Y, ref) <= BF16_TOL
+    assert canaries_intact(buf, (M, N))
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 4096, 1280), (37, 2048, 96), (300, 1024, 264)])
+def test_linear_col_bf16_fp32_partial_out(M, K, N):
+    """bf16 inputs with fp32 outputs (the row layer's fp32-partial option) are tighter."""
+    log_case("row partial fp32 out", M, K, N)
+    x, w = I.activations(M, K, 5), I.weight(N, K, 6)
+    P = torch.empty(M, N, device="cuda", dtype=torch.float32)
+    tp.tp_linear_row_partial(dev(x), K, dev(w), P, M, K, N, 1)
+    torch.cuda.synchronize()
+    assert err(P, O.linear(host64(x), host64(w))) <= 1e-5
+
+
+@pytest.mark.parametrize("M", [1, 3, 64, 200])
+@pytest.mark.parametrize("p", [2, 4])
+def test_row_partial_rank_slices_sum(M, p):
+    """Row split with the rank's slice of a full X (ldx = K) and the bias added once."""
+    log_case("row split sum", M, p)
+    K, N = 1024, 320
+    x, w, b = I.activations(M, K, 11), I.weight(N, K, 12), I.bias(N, 13)
+    X, W = dev(x), dev(w)
+    parts = []
+    for r in range(p):
+        W_r = torch.empty(N, K // p, dtype=torch.bfloat16, device="cuda")
+        tp.tp_shard_weight(W, N, K, p, r, 1, W_r)
+        P_r = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        tp.tp_linear_row_partial(X[:, r * (K // p):], K, W_r, P_r, M, K, N, p)
+        parts.append(P_r)
+        ref_r = O.row_partial(O.input_slice(host64(x), p, r), O.row_shard(host64(w), p, r))
+        torch.cuda.synchronize()
+        assert err(P_r, ref_r) <= BF16_TOL
+    Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    tp.tp_combine_sum(parts, dev(b), Y, M, N)
+    torch.cuda.synchronize()
+    assert err(Y, O.linear(host64(x), host64(w), host64(b))) <= BF16_TOL
+
+
+# ---- SwiGLU MLP shard -------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bias", [False, True])
+@pytest.mark.parametrize("M", [1, 7, 16, 40, 64, 65, 300])
+def test_mlp_shard_bf16(M, bias):
+    log_case("mlp shard", M, bias)
+    h, inter, p = 1024, 3072, 2
+    shape = I.LayerShape("t", hidden=h, intermediate=inter, tp=p, seed=40 + M)
+    wt = I.ffn_weights(shape, with_bias=bias)
+    x = I.activations(M, h, 41 + M)
+    X = dev(x)
+    parts = []
+    hs = []
+    for r in range(p):
+        Wg_r, bg_r = O.col_shard(host64(wt["Wg"]), host64(wt["bg"]) if bias else None, p, r)
+        i = inter // p
+        sl = slice(r * i, (r + 1) * i)
+        H_r = torch.empty(M, i, dtype=torch.bfloat16, device="cuda")
+        P_r = torch.empty(M, h, dtype=torch.bfloat16, device="cuda")
+        tp.tp_mlp_shard(X, dev(wt["Wg"][sl]), dev(wt["Wu"][sl]),
+                        dev(wt["bg"][sl]) if bias else None, dev(wt["bu"][sl]) if bias else None,
+                        dev(wt["Wd"][:, sl]), H_r, P_r, M, h, inter, p)
+        torch.cuda.synchronize()
+        h_ref, p_ref = O.mlp_shard(host64(x), Wg_r, host64(wt["Wu"][sl]), host64(wt["Wd"][:, sl]),
+                                   bg_r, host64(wt["bu"][sl]) if bias else None)
+        assert err(H_r, h_ref) <= BF16_TOL
+        # the partial is checked against the oracle applied to the GPU's own bf16 H_r
+        assert err(P_r, O.row_partial(host64(H_r), host64(wt["Wd"][:, sl]))) <= BF16_TOL
+        assert err(P_r, p_ref) <= BF16_TOL
+        parts.append(P_r)
+        hs.append(H_r)
+    Y = torch.empty(M, h, dtype=torch.bfloat16, device="cuda")
+    tp.tp_combine_sum(parts, dev(wt["bd"]) if bias else None, Y, M, h)
+    Hc = torch.empty(M, inter, dtype=torch.bfloat16, device="cuda")
+    tp.tp_combine_concat(hs, [inter // p], Hc, M)
+    torch.cuda.synchronize()
+    w64 = {k: host64(v) for k, v in wt.items()}
+    ref = O.mlp(host64(x), w64["Wg"], w64["Wu"], w64["Wd"], w64.get("bg"), w64.get("bu"), w64.get("bd"))
+    assert err(Y, ref) <= BF16_TOL
+    h_full = O.swiglu(O.linear(host64(x), w64["Wg"], w64.get("bg")), O.linear(host64(x), w64["Wu"], w64.get("bu")))
+    assert err(Hc, h_full) <= BF16_TOL
+
+
+def test_mlp_shard_fp32_and_skip_down():
+    log_case("mlp shard fp32")
+    M, h, inter, p = 5, 64, 96, 2
+    shape = I.LayerShape("t", hidden=h, intermediate=inter, tp=p, seed=50)
+    wt = I.ffn_weights(shape, dtype=torch.float32)
+    x = I.activations(M, h, 51, dtype=torch.float32)
+    i = inter // p
+    H_r = torch.empty(M, i, device="cuda")
+    tp.tp_mlp_shard(dev(x), dev(wt["Wg"][:i]), dev(wt["Wu"][:i]), dev(wt["bg"][:i]), dev(wt["bu"][:i]),
+                    None, H_r, None, M, h, inter, p)
+    torch.cuda.synchronize()
+    w64 = {k: host64(v) for k, v in wt.items()}
+    ref = O.swiglu(O.linear(host64(x), w64["Wg"][:i], w64["bg"][:i]), O.linear(host64(x), w64["Wu"][:i], w64["bu"][:i]))
+    assert err(H_r, ref) <= F32_TOL
+
+
+# ---- head-split attention projections ----------------------------------------------------------
+
+@pytest.mark.parametrize("M", [1, 9, 130])
+def test_attn_proj_shards_and_combines(M):
+    log_case("attn proj", M)
+    nh, nkv, d, h, p = 16, 4, 32, 512, 4
+    shape = I.LayerShape("t", hidden=h, n_heads=nh, n_kv_heads=nkv, head_dim=d, tp=p, seed=60 + M)
+    wt = I.attn_weights(shape)
+    x = I.activations(M, h, 61 + M)
+    a_full = I.activations(M, nh * d, 62 + M)
+    Wqkv, bqkv, Wo = dev(wt["Wqkv"]), dev(wt["bqkv"]), dev(wt["Wo"])
+    nq = (nh // p + 2 * nkv // p) * d
+    ka = nh // p * d
+    qkvs, parts = [], []
+    for r in range(p):
+        W_r = torch.empty(nq, h, dtype=torch.bfloat16, device="cuda")
+        b_r = torch.empty(nq, dtype=torch.bfloat16, device="cuda")
+        Wo_r = torch.empty(h, ka, dtype=torch.bfloat16, device="cuda")
+        tp.tp_shard_qkv(Wqkv, h, nh, nkv, d, p, r, W_r)
+        tp.tp_shard_qkv(bqkv, 1, nh, nkv, d, p, r, b_r)
+        tp.tp_shard_weight(Wo, h, nh * d, p, r, 1, Wo_r)
+        QKV_r = torch.empty(M, nq, dtype=torch.bfloat16, device="cuda")
+        P_r = torch.empty(M, h, dtype=torch.bfloat16, device="cuda")
+        A_r = dev(a_full[:, r * ka:(r + 1) * ka])
+        tp.tp_attn_proj_shard(dev(x), W_r, b_r, QKV_r, A_r, Wo_r, P_r, M, h, nh, nkv, d, p)
+        torch.cuda.synchronize()
+        w_ref, b_ref = O.qkv_shard(host64(wt["Wqkv"]), host64(wt["bqkv"]), nh, nkv, d, p, r)
+        np.testing.assert_array_equal(host64(W_r), w_ref)   # the head split itself is exact
+        np.testing.assert_array_equal(host64(b_r), b_ref)
+        assert err(QKV_r, O.col_linear(host64(x), w_ref, b_ref)) <= BF16_TOL
+        assert err(P_r, O.row_partial(host64(a_full)[:, r * ka:(r + 1) * ka], O.row_shard(host64(wt["Wo"]), p, r))) <= BF16_TOL
+        qkvs.append(QKV_r)
+        parts.append(P_r)
+    QKV = torch.empty(M, (nh + 2 * nkv) * d, dtype=torch.bfloat16, device="cuda")
+    seg = O.qkv_segments(nh, nkv, d, p)
+    tp.tp_combine_concat(qkvs, list(seg), QKV, M)
+    Y = torch.empty(M, h, dtype=torch.bfloat16, device="cuda")
+    tp.tp_combine_sum(parts, dev(wt["bo"]), Y, M, h)
+    torch.cuda.synchronize()
+    assert err(QKV, O.linear(host64(x), host64(wt["Wqkv"]), host64(wt["bqkv"]))) <= BF16_TOL
+    assert err(Y, O.linear(host64(a_full), host64(wt["Wo"]), host64(wt["bo"]))) <= BF16_TOL
+    # concat is a pure copy: bit-exact against the oracle's segment concat of the GPU shards
+    np.testing.assert_array_equal(host64(QKV), O.concat([host64(q) for q in qkvs], seg))
+
+
+# ---- combines: exactness, dtypes, ragged sizes ---------------------------------------------
+
+@pytest.mark.parametrize("pdt,odt", [(torch.bfloat16, torch.bfloat16), (torch.float32, torch.bfloat16),
+                                     (torch.float32, torch.float32), (torch.bfloat16, torch.float32)])
+@pytest.mark.parametrize("M,N,p", [(1, 8, 2), (3, 13, 3), (7, 4096, 8), (5, 1000, 4)])
+def test_combine_sum(M, N, p, pdt, odt):
+    log_case("combine sum", M, N, p, pdt, odt)
+    parts = [I.activations(M, N, 70 + r, dtype=torch.float32).to(pdt) for r in range(p)]
+    b = I.bias(N, 79, dtype=torch.float32).to(odt)
+    Y = torch.empty(M, N, dtype=odt, device="cuda")
+    tp.tp_combine_sum([dev(t) for t in parts], dev(b), Y, M, N)
+    torch.cuda.synchronize()
+    ref = O.combine_sum([host64(t) for t in parts], host64(b))
+    tol = BF16_TOL if odt == torch.bfloat16 else 1e-6
+    assert err(Y, ref) <= tol
+    # the same fp32 accumulation order on the host gives the identical fp32 result
+    if odt == torch.float32:
+        acc = torch.zeros(M, N, dtype=torch.float32)
+        for t in parts:
+            acc = acc + t.float()
+        acc = acc + b.float()
+        assert torch.equal(acc, Y.cpu())
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("M,segs,p", [(1, [3], 2), (4, [5, 4], 2), (6, [1024, 128, 128], 8), (3, [7], 3)])
+def test_combine_concat_exact(M, segs, p, dtype):
+    log_case("concat", M, segs, p, dtype)
+    s = sum(segs)
+    shards = [I.activations(M, s, 90 + r, dtype=torch.float32).to(dtype) for r in range(p)]
+    Y = torch.empty(M, p * s, dtype=dtype, device="cuda")
+    tp.tp_combine_concat([dev(t) for t in shards], segs, Y, M)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host64(Y), O.concat([host64(t) for t in shards], segs))
+
+
+def test_uneven_split_five_plus_four_via_concat():
+    """'Try it yourself' on the GPU: 9 outputs as shards of 5 and 4, each computed as a
+    column product, then concatenated (the ABI's even split is bypassed with p = 1 calls)."""
+    log_case("uneven 5+4")
+    x, w, b = I.toy_layer_uneven(9)
+    X = dev(x)
+    outs = []
+    for lo, hi in ((0, 5), (5, 9)):
+        Y_r = torch.empty(1, hi - lo, device="cuda")
+        tp.tp_linear_col(X, dev(w[lo:hi]), dev(b[lo:hi]), Y_r, 1, 8, hi - lo, 1)
+        outs.append(Y_r)
+    torch.cuda.synchronize()
+    got = np.concatenate([host64(o) for o in outs], axis=-1)
+    assert O.rel_err(got, O.linear(host64(x), host64(w), host64(b))) <= F32_TOL
+
+
+def test_shard_weight_exact():
+    log_case("shard weight")
+    w = I.weight(48, 40, 99)
+    W = dev(w)
+    for p in (1, 2, 4, 8):
+        for r in range(p):
+            c = torch.empty(48 // p, 40, dtype=torch.bfloat16, device="cuda")
+            tp.tp_shard_weight(W, 48, 40, p, r, 0, c)
+            rr = torch.empty(48, 40 // p if 40 % p == 0 else 1, dtype=torch.bfloat16, device="cuda")
+            if 40 % p == 0:
+                tp.tp_shard_weight(W, 48, 40, p, r, 1, rr)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(host64(c), O.col_shard(host64(w), None, p, r)[0])
+            if 40 % p == 0:
+                np.testing.assert_array_equal(host64(rr), O.row_shard(host64(w), p, r))
+
+
+# ---- determinism, M = 0, error path on the device ------------------------------------------
+
+@pytest.mark.parametrize("M,K,N", [(1, 8192, 1280), (64, 4096, 688), (300, 2048, 520)])
+def test_bitwise_deterministic(M, K, N):
+    log_case("deterministic", M, K, N)
+    x, w, b = I.activations(M, K, 1), I.weight(N, K, 2), I.bias(N, 3)
+    X, W, B = dev(x), dev(w), dev(b)
+    Y1 = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    Y2 = torch.empty_like(Y1)
+    tp.tp_linear_col(X, W, B, Y1, M, K, N, 1)
+    tp.tp_linear_col(X, W, B, Y2, M, K, N, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(Y1, Y2)
+
+
+def test_zero_tokens_is_a_no_op():
+    Y = torch.full((4, 16), 7.0, dtype=torch.bfloat16, device="cuda")
+    W = torch.zeros(16, 8, dtype=torch.bfloat16, device="cuda")
+    X = torch.zeros(1, 8, dtype=torch.bfloat16, device="cuda")
+    tp.tp_linear_col(X, W, None, Y, 0, 8, 16, 1)
+    torch.cuda.synchronize()
+    assert bool((Y == 7.0).all())
+
+
+def test_errors_raise_before_launch():
+    X = torch.zeros(2, 4096, dtype=torch.bfloat16, device="cuda")
+    W = torch.zeros(11008 // 2, 4096, dtype=torch.bfloat16, device="cuda")
+    Y = torch.zeros(2, 11008 // 2, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(tp.TPError) as e:
+        tp.tp_linear_col(X, W, None, Y, 2, 4096, 11008, 3)
+    assert e.value.status == 3
