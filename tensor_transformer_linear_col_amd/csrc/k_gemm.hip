@@ -9,8 +9,10 @@
 //     global loads of slice k+1 are in flight (in registers) while the matrix
 //     cores consume slice k, and one barrier per slice separates the buffers;
 //   * stores each 128-byte LDS row as 8 chunks of 16 bytes placed at chunk
-//     c ^ (row & 7), so both the row-wise stores and the column-wise MFMA operand
-//     reads hit 8 distinct bank groups;
+//     c ^ ((row >> 1) & 7): gfx950 serves a 16-byte-per-lane LDS access 16 lanes
+//     (256 bytes, all 64 banks) at a time, and with this placement both the
+//     row-wise stores (2 rows x 8 chunks) and the MFMA operand reads (16
+//     consecutive rows, one chunk each) cover 16 distinct 16-byte bank groups;
 //   * for SwiGLU keeps the gate rows and the up rows of the same intermediate
 //     features in one tile, so the epilogue has both sums in registers;
 //   * orders tiles so that the workgroups resident on one XCD (the hardware deals
@@ -58,8 +60,9 @@ __device__ __forceinline__ void tile_of(int b, int tiles_n, int tiles_m, int& tn
     tm = rem / gw;
 }
 
-template <int TN, int TM, int WAVES_N, int WAVES_M, bool SWIGLU, bool BIAS, typename OutT>
-__global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void gemm_kernel(GemmParams p) {
+template <int TN, int TM, int WAVES_N, int WAVES_M, bool SWIGLU, bool BIAS, bool KTAIL, typename OutT>
+__global__ __launch_bounds__(WAVES_N* WAVES_M * 64)
+__attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_kernel(GemmParams p) {
     constexpr int NT = WAVES_N * WAVES_M * 64;
     constexpr int WN = TN / WAVES_N;           // output features per wave
     constexpr int WM = TM / WAVES_M;           // tokens per wave
@@ -67,10 +70,11 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void gemm_kernel(GemmParams 
     constexpr int NA = SWIGLU ? 2 * BN : BN;   // A-operand blocks (gate then up)
     constexpr int WROWS = SWIGLU ? 2 * TN : TN;
     constexpr int ROWS = WROWS + TM;  // LDS rows per stage
-    constexpr int CHUNKS = ROWS * 8;  // 16-byte chunks per stage
-    constexpr int LPT = CHUNKS / NT;  // chunks per thread per stage
+    constexpr int RSTEP = NT / 8;     // rows covered by one round of 16-byte chunk loads
+    constexpr int LW = WROWS / RSTEP, LX = TM / RSTEP, LPT = LW + LX;
     static_assert(WN % 32 == 0 && WM % 32 == 0, "wave tile must be whole 32x32 blocks");
-    static_assert(CHUNKS % NT == 0, "stage must split evenly over the threads");
+    static_assert(WROWS % RSTEP == 0 && TM % RSTEP == 0 && TN % RSTEP == 0, "rounds must not straddle operands");
+    static_assert(RSTEP % 16 == 0, "the LDS swizzle must repeat every round");
 
     __shared__ __attribute__((aligned(16))) bf16 lds[2][ROWS * BK];
 
@@ -84,38 +88,48 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void gemm_kernel(GemmParams 
     tile_of(blockIdx.x, p.tiles_n, p.tiles_m, tn, tm);
     const int n0 = tn * TN, m0 = tm * TM;
 
-    // This thread's global chunks. Rows past N / tokens past M are clamped to the
-    // last valid row; their products land in outputs that are never stored.
-    const bf16* src[LPT];
-    int kcol[LPT];
-    int dst[LPT];
+    // Global side: thread t loads chunk c = t % 8 of rows t / 8 + i * RSTEP. Rows past
+    // N / tokens past M are clamped to the last valid row; their products land in
+    // outputs that are never stored. Offsets are bytes from the operand's base
+    // (each operand is below 4 GiB, checked on the host).
+    const int c = tid & 7, r0 = tid >> 3;
+    uint32_t off[LPT];
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-        const int q = tid + i * NT;
-        const int row = q >> 3, c = q & 7;
-        if (row < WROWS) {
-            const bool up = SWIGLU && row >= TN;
-            const int n = min(n0 + (up ? row - TN : row), p.N - 1);
-            src[i] = (up ? p.W1 : p.W0) + (int64_t)n * p.K + c * 8;
-        } else {
-            const int m = min(m0 + row - WROWS, p.M - 1);
-            src[i] = p.X + (int64_t)m * p.ldx + c * 8;
-        }
-        kcol[i] = c * 8;
-        dst[i] = row * BK + ((c ^ (row & 7)) * 8);
+    for (int i = 0; i < LW; ++i) {
+        const int row = r0 + i * RSTEP;
+        const bool up = SWIGLU && row >= TN;
+        const int n = min(n0 + (up ? row - TN : row), p.N - 1);
+        off[i] = (uint32_t)(((int64_t)n * p.K + c * 8) * 2);
     }
+#pragma unroll
+    for (int i = 0; i < LX; ++i) {
+        const int m = min(m0 + r0 + i * RSTEP, p.M - 1);
+        off[LW + i] = (uint32_t)(((int64_t)m * p.ldx + c * 8) * 2);
+    }
+    // LDS side: row r0 + i*RSTEP, chunk c stored at c ^ ((row >> 1) & 7); the swizzle
+    // term is the same for every round because RSTEP is a multiple of 16.
+    const int dst0 = r0 * BK + ((c ^ ((r0 >> 1) & 7)) * 8);
 
+    const char* w0b = reinterpret_cast<const char*>(p.W0);
+    const char* w1b = reinterpret_cast<const char*>(SWIGLU ? p.W1 : p.W0);
+    const char* xb = reinterpret_cast<const char*>(p.X);
     const int KT = (p.K + BK - 1) / BK;
-    bf16x8 pre[LPT];
-    const bf16x8 zero = {};
-    auto load_stage = [&](int kt) {
-        const int k0 = kt * BK;
+    auto load_stage = [&](int kt, bf16x8 (&pre)[LPT]) {
+        const int64_t kb = (int64_t)kt * BK * 2;
 #pragma unroll
-        for (int i = 0; i < LPT; ++i) pre[i] = (k0 + kcol[i] < p.K) ? ld8g(src[i] + k0) : zero;
+        for (int i = 0; i < LPT; ++i) {
+            const char* base = i < LW ? ((SWIGLU && i * RSTEP >= TN) ? w1b : w0b) : xb;
+            const char* a = base + kb + off[i];
+            if (KTAIL) a -= (kt * BK + c * 8 >= p.K) ? kb : 0;  // past K: re-read column 0, zeroed below
+            pre[i] = *reinterpret_cast<const bf16x8*>(a);
+        }
     };
-    auto store_stage = [&](int buf) {
+    auto store_stage = [&](int kt, int buf, bf16x8 (&pre)[LPT]) {
+        const bool ok = !KTAIL || kt * BK + c * 8 < p.K;
+        const bf16x8 zero = {};
 #pragma unroll
-        for (int i = 0; i < LPT; ++i) *reinterpret_cast<bf16x8*>(&lds[buf][dst[i]]) = pre[i];
+        for (int i = 0; i < LPT; ++i)
+            *reinterpret_cast<bf16x8*>(&lds[buf][dst0 + i * RSTEP * BK]) = ok ? pre[i] : zero;
     };
 
     floatx16 acc[NA][BM];
@@ -126,44 +140,62 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void gemm_kernel(GemmParams 
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    // LDS rows read by this lane for each A / B block.
-    int arow[NA], brow[BM];
+    // MFMA operand reads. Every block starts on a multiple of 32 rows, so the swizzle
+    // term of this lane's row is (l32 >> 1) & 7 for all of them.
+    const int sw = (l32 >> 1) & 7;
+    const int lrow = l32 * BK;
+    int arow[NA];
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
         const bool up = SWIGLU && i >= BN;
-        arow[i] = (up ? TN : 0) + wn * WN + (up ? i - BN : i) * 32 + l32;
+        arow[i] = ((up ? TN : 0) + wn * WN + (up ? i - BN : i) * 32) * BK;
     }
+    const int brow0 = (WROWS + wm * WM) * BK;
+    auto read_frags = [&](const bf16* s, int ks, bf16x8 (&af)[NA], bf16x8 (&bfr)[BM]) {
+        const int kx = (((2 * ks + lh) ^ sw) * 8) + lrow;
 #pragma unroll
-    for (int j = 0; j < BM; ++j) brow[j] = WROWS + wm * WM + j * 32 + l32;
-
-    auto compute = [&](int buf) {
-        const bf16* s = lds[buf];
+        for (int i = 0; i < NA; ++i) af[i] = *reinterpret_cast<const bf16x8*>(&s[arow[i] + kx]);
 #pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            const int c = 2 * ks + lh;
-            bf16x8 af[NA], bfr[BM];
+        for (int j = 0; j < BM; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(&s[brow0 + j * 32 * BK + kx]);
+    };
+    auto mfmas = [&](bf16x8 (&af)[NA], bf16x8 (&bfr)[BM]) {
 #pragma unroll
-            for (int i = 0; i < NA; ++i)
-                af[i] = *reinterpret_cast<const bf16x8*>(&s[arow[i] * BK + ((c ^ (arow[i] & 7)) * 8)]);
+        for (int i = 0; i < NA; ++i)
 #pragma unroll
             for (int j = 0; j < BM; ++j)
-                bfr[j] = *reinterpret_cast<const bf16x8*>(&s[brow[j] * BK + ((c ^ (brow[j] & 7)) * 8)]);
-#pragma unroll
-            for (int i = 0; i < NA; ++i)
-#pragma unroll
-                for (int j = 0; j < BM; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-        }
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    };
+    // The fragments of sub-step ks+1 are requested before the MFMAs of sub-step ks are
+    // issued; the scheduling barriers keep the compiler from sinking those reads next
+    // to their use, which would expose the LDS latency with one wave per SIMD.
+    auto compute = [&](int buf) {
+        const bf16* s = lds[buf];
+        bf16x8 fa0[NA], fb0[BM], fa1[NA], fb1[BM];
+        read_frags(s, 0, fa0, fb0);
+        read_frags(s, 1, fa1, fb1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(fa0, fb0);
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(s, 2, fa0, fb0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(fa1, fb1);
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(s, 3, fa1, fb1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(fa0, fb0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(fa1, fb1);
     };
 
-    load_stage(0);
-    store_stage(0);
+    bf16x8 pre[LPT];
+    load_stage(0, pre);
+    store_stage(0, 0, pre);
     __syncthreads();
     for (int kt = 0; kt < KT; ++kt) {
         const bool more = kt + 1 < KT;
-        if (more) load_stage(kt + 1);
+        if (more) load_stage(kt + 1, pre);
         compute(kt & 1);
-        if (more) store_stage((kt + 1) & 1);
+        if (more) store_stage(kt + 1, (kt + 1) & 1, pre);
         __syncthreads();
     }
 
@@ -183,10 +215,239 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void gemm_kernel(GemmParams 
                 const int n_base = n0 + wn * WN + i * 32 + 8 * q + 4 * lh;
                 const int m = m0 + wm * WM + j * 32 + l32;
                 epilogue4<SWIGLU, BIAS, OutT>(p.o, n_base, m, gv, uv);
+                __builtin_amdgcn_sched_barrier(0);  // keep bias loads next to their use
+            }
+}
+
+// ---------------------------------------------------------------------------------
+// Large-tile kernel with direct global -> LDS loads.
+//
+// gfx950's global_load_lds_dwordx4 writes each lane's 16 bytes straight into LDS
+// (at a wave-uniform LDS address + 16 * lane), so staging needs no registers and
+// the LDS ring can hold four 32-wide K slices: three are in flight while the
+// matrix cores consume the fourth (a fifth slice, all 160 KB, measured no faster). Holding more than one slice in registers
+// would not fit next to the 128 x 128 accumulator tile of each wave.
+//
+// LDS row = 32 bf16 = 64 bytes = 4 chunks of 16 bytes; chunk c of row r is stored
+// at position c ^ ((r >> 2) & 3). A DMA instruction fills 16 consecutive rows
+// (1 KB, 4 lanes per row, each lane fetching the chunk that belongs at its
+// position), and an MFMA operand read (16 lanes = 16 consecutive rows, one chunk)
+// touches 16 distinct 16-byte bank groups.
+//
+// Synchronisation is explicit: before slice k is read, each wave waits until its
+// own DMA for slice k has landed (vmcnt, loads complete in order), then all waves
+// meet at s_barrier; only then is slice k+3 requested into the buffer that held
+// slice k-1, which every wave has finished reading.
+// ---------------------------------------------------------------------------------
+constexpr int DBK = 32;      // K slice per stage
+#ifndef TP_DMA_STAGES
+#define TP_DMA_STAGES 4
+#endif
+#ifndef TP_DMA_WAVES_M
+#define TP_DMA_WAVES_M 2
+#endif
+constexpr int DSTAGES = TP_DMA_STAGES;  // LDS ring depth (4 x 32 KB)
+
+constexpr unsigned vmcnt_wait(int n) {  // s_waitcnt immediate: vmcnt(n), no other wait
+    return (unsigned)((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ __forceinline__ void dma16(const char* g, char* l) {
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(g), (__attribute__((address_space(3))) void*)l, 16,
+                                     0, 0);
+}
+
+template <int TN, int TM, int WAVES_N, int WAVES_M, bool SWIGLU, bool BIAS, typename OutT>
+__global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void gemm_dtl_kernel(GemmParams p) {
+    constexpr int NWAVES = WAVES_N * WAVES_M;
+    constexpr int WN = TN / WAVES_N, WM = TM / WAVES_M;
+    constexpr int BN = WN / 32, BM = WM / 32;
+    constexpr int NA = SWIGLU ? 2 * BN : BN;
+    constexpr int WROWS = SWIGLU ? 2 * TN : TN;
+    constexpr int ROWS = WROWS + TM;
+    constexpr int ROWB = DBK * 2;              // bytes per LDS row
+    constexpr int STAGEB = ROWS * ROWB;
+    constexpr int IPW = ROWS / 16 / NWAVES;    // DMA instructions per wave per stage
+    static_assert(WN % 32 == 0 && WM % 32 == 0, "wave tile must be whole 32x32 blocks");
+    static_assert(ROWS % 64 == 0 && (IPW * 16) % 16 == 0, "each wave fills whole 16-row groups");
+    static_assert((TN % (IPW * 16)) == 0 && (WROWS % (IPW * 16)) == 0, "a wave's rows come from one operand");
+
+    __shared__ __attribute__((aligned(1024))) char lds[DSTAGES][STAGEB];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wn = wave % WAVES_N, wm = wave / WAVES_N;
+    const int l32 = lane & 31, lh = lane >> 5;
+
+    int tn, tm;
+    tile_of(blockIdx.x, p.tiles_n, p.tiles_m, tn, tm);
+    const int n0 = tn * TN, m0 = tm * TM;
+
+    // This wave's DMA rows: (wave * IPW + j) * 16 + lane / 4, all from one operand.
+    const int wrow0 = wave * IPW * 16;
+    const char* gbase;
+    if (wrow0 < WROWS) {
+        const bool up = SWIGLU && wrow0 >= TN;
+        gbase = reinterpret_cast<const char*>(up ? p.W1 : p.W0);
+    } else {
+        gbase = reinterpret_cast<const char*>(p.X);
+    }
+    uint32_t goff[IPW];
+#pragma unroll
+    for (int j = 0; j < IPW; ++j) {
+        const int row = wrow0 + j * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ ((row >> 2) & 3);  // the chunk that belongs at this lane's position
+        if (wrow0 < WROWS) {
+            const bool up = SWIGLU && row >= TN;
+            const int n = min(n0 + (up ? row - TN : row), p.N - 1);
+            goff[j] = (uint32_t)(((int64_t)n * p.K + c * 8) * 2);
+        } else {
+            const int m = min(m0 + row - WROWS, p.M - 1);
+            goff[j] = (uint32_t)(((int64_t)m * p.ldx + c * 8) * 2);
+        }
+    }
+    const int KT = p.K / DBK;
+    auto issue_stage = [&](int kt, int buf) {
+        const char* g = gbase + (int64_t)kt * DBK * 2;
+        char* l = &lds[buf][wrow0 * ROWB];
+#pragma unroll
+        for (int j = 0; j < IPW; ++j) dma16(g + goff[j], l + j * 1024);
+    };
+
+    floatx16 acc[NA][BM];
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+#pragma unroll
+        for (int j = 0; j < BM; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+    // Operand reads: every block starts on a multiple of 32 rows, so this lane's
+    // swizzle term is (l32 >> 2) & 3 for all of them.
+    const int sw = (l32 >> 2) & 3;
+    int arow[NA];
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+        const bool up = SWIGLU && i >= BN;
+        arow[i] = ((up ? TN : 0) + wn * WN + (up ? i - BN : i) * 32) * ROWB;
+    }
+    const int brow0 = (WROWS + wm * WM) * ROWB;
+    auto read_frags = [&](const char* s, int ks, bf16x8 (&af)[NA], bf16x8 (&bfr)[BM]) {
+        const int kx = l32 * ROWB + (((2 * ks + lh) ^ sw) * 16);
+#pragma unroll
+        for (int i = 0; i < NA; ++i) af[i] = *reinterpret_cast<const bf16x8*>(s + arow[i] + kx);
+#pragma unroll
+        for (int j = 0; j < BM; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(s + brow0 + j * 32 * ROWB + kx);
+    };
+    auto mfmas = [&](bf16x8 (&af)[NA], bf16x8 (&bfr)[BM]) {
+#pragma unroll
+        for (int i = 0; i < NA; ++i)
+#pragma unroll
+            for (int j = 0; j < BM; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    };
+
+    // Wait until this wave's DMA for slice k has landed (DMA completes in order; `ahead`
+    // slices were requested after it), then meet the other waves.
+    auto sync_slice = [&](int ahead) {
+        static_assert(DSTAGES <= 5, "waits below cover up to 3 slices ahead");
+        if (ahead >= 3) __builtin_amdgcn_s_waitcnt(vmcnt_wait(3 * IPW));
+        else if (ahead == 2) __builtin_amdgcn_s_waitcnt(vmcnt_wait(2 * IPW));
+        else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vmcnt_wait(IPW));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));  // also for a slice past the end
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    };
+
+    // Prologue: slices 0 .. DSTAGES-2 requested; sub-step 0 of slice 0 read.
+    for (int s = 0; s < DSTAGES - 1 && s < KT; ++s) issue_stage(s, s);
+    sync_slice(min(KT - 1, DSTAGES - 2));
+    bf16x8 fa0[NA], fb0[BM], fa1[NA], fb1[BM];
+    read_frags(lds[0], 0, fa0, fb0);
+    // Nothing but these LDS reads may be pending on lgkmcnt when the loop starts, so
+    // the waits inside it can count in-order LDS returns.
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    // Per slice k: read sub-step 1 | MFMAs of sub-step 0 | barrier for slice k+1 and
+    // request slice k+DSTAGES-1 into slice k-1's buffer | read sub-step 0 of slice k+1 |
+    // MFMAs of sub-step 1. Every LDS read has one MFMA phase to land.
+    // lgkmcnt has 4 bits: with two batches of 8 reads outstanding the compiler could
+    // only wait for zero. Each batch is therefore drained (it had a whole MFMA phase
+    // to land, so this does not stall) before the next one is issued.
+    for (int kt = 0; kt < KT; ++kt) {
+        const char* s = lds[kt % DSTAGES];
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): sub-step 0 of slice k is in
+        read_frags(s, 1, fa1, fb1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(fa0, fb0);
+        __builtin_amdgcn_sched_barrier(0);
+        // Unconditional, so every path into the MFMAs below is the same. On the last
+        // slice this synchronises once more and reads a buffer nobody uses any more.
+        sync_slice(min(KT - 2 - kt, DSTAGES - 3));
+        if (kt + DSTAGES - 1 < KT) issue_stage(kt + DSTAGES - 1, (kt + DSTAGES - 1) % DSTAGES);
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): sub-step 1 of slice k is in
+        read_frags(lds[(kt + 1) % DSTAGES], 0, fa0, fb0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(fa1, fb1);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+#pragma unroll
+    for (int i = 0; i < BN; ++i)
+#pragma unroll
+        for (int j = 0; j < BM; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float gv[4], uv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    gv[e] = acc[i][j][4 * q + e];
+                    uv[e] = SWIGLU ? acc[i + (SWIGLU ? BN : 0)][j][4 * q + e] : 0.f;
+                }
+                const int n_base = n0 + wn * WN + i * 32 + 8 * q + 4 * lh;
+                const int m = m0 + wm * WM + j * 32 + l32;
+                epilogue4<SWIGLU, BIAS, OutT>(p.o, n_base, m, gv, uv);
+                __builtin_amdgcn_sched_barrier(0);
             }
 }
 
 template <int TN, int TM, int WAVES_N, int WAVES_M, bool SWIGLU, bool BIAS, typename OutT>
+tp_status_t run_dtl(const LinearDesc& d, hipStream_t stream) {
+    GemmParams p;
+    p.X = static_cast<const bf16*>(d.X);
+    p.ldx = d.ldx;
+    p.W0 = static_cast<const bf16*>(d.W0);
+    p.W1 = static_cast<const bf16*>(d.W1);
+    p.o.Y = d.Y;
+    p.o.ldy = d.ldy;
+    p.o.M = (int)d.M;
+    p.o.N = (int)d.N;
+    p.o.b0 = static_cast<const bf16*>(d.b0);
+    p.o.b1 = static_cast<const bf16*>(d.b1);
+    p.o.vec_store = vec_store_ok<OutT>(d.Y, d.ldy);
+    p.M = (int)d.M;
+    p.N = (int)d.N;
+    p.K = (int)d.K;
+    p.tiles_n = (int)ceil_div(d.N, TN);
+    p.tiles_m = (int)ceil_div(d.M, TM);
+    const int64_t tiles = (int64_t)p.tiles_n * p.tiles_m;
+    hipLaunchKernelGGL((gemm_dtl_kernel<TN, TM, WAVES_N, WAVES_M, SWIGLU, BIAS, OutT>), dim3((unsigned)tiles),
+                       dim3(WAVES_N * WAVES_M * 64), 0, stream, p);
+    return hip_status();
+}
+
+template <int TN, int TM, int WAVES_N, int WAVES_M, bool SWIGLU>
+tp_status_t run_dtl_bias(const LinearDesc& d, hipStream_t stream) {
+    const bool bias = d.b0 != nullptr;
+    if (d.out_dtype == TP_DTYPE_BF16)
+        return bias ? run_dtl<TN, TM, WAVES_N, WAVES_M, SWIGLU, true, bf16>(d, stream)
+                    : run_dtl<TN, TM, WAVES_N, WAVES_M, SWIGLU, false, bf16>(d, stream);
+    return bias ? run_dtl<TN, TM, WAVES_N, WAVES_M, SWIGLU, true, float>(d, stream)
+                : run_dtl<TN, TM, WAVES_N, WAVES_M, SWIGLU, false, float>(d, stream);
+}
+
+template <int TN, int TM, int WAVES_N, int WAVES_M, bool SWIGLU, bool BIAS, bool KTAIL, typename OutT>
 tp_status_t run(const LinearDesc& d, hipStream_t stream) {
     GemmParams p;
     p.X = static_cast<const bf16*>(d.X);
@@ -206,24 +467,34 @@ tp_status_t run(const LinearDesc& d, hipStream_t stream) {
     p.tiles_n = (int)ceil_div(d.N, TN);
     p.tiles_m = (int)ceil_div(d.M, TM);
     const int64_t tiles = (int64_t)p.tiles_n * p.tiles_m;
-    hipLaunchKernelGGL((gemm_kernel<TN, TM, WAVES_N, WAVES_M, SWIGLU, BIAS, OutT>), dim3((unsigned)tiles),
+    hipLaunchKernelGGL((gemm_kernel<TN, TM, WAVES_N, WAVES_M, SWIGLU, BIAS, KTAIL, OutT>), dim3((unsigned)tiles),
                        dim3(WAVES_N * WAVES_M * 64), 0, stream, p);
     return hip_status();
+}
+
+template <int TN, int TM, int WAVES_N, int WAVES_M, bool SWIGLU, bool BIAS, bool KTAIL>
+tp_status_t run_out(const LinearDesc& d, hipStream_t stream) {
+    return d.out_dtype == TP_DTYPE_BF16 ? run<TN, TM, WAVES_N, WAVES_M, SWIGLU, BIAS, KTAIL, bf16>(d, stream)
+                                        : run<TN, TM, WAVES_N, WAVES_M, SWIGLU, BIAS, KTAIL, float>(d, stream);
 }
 
 template <int TN, int TM, int WAVES_N, int WAVES_M, bool SWIGLU>
 tp_status_t run_bias(const LinearDesc& d, hipStream_t stream) {
     const bool bias = d.b0 != nullptr;
-    if (d.out_dtype == TP_DTYPE_BF16)
-        return bias ? run<TN, TM, WAVES_N, WAVES_M, SWIGLU, true, bf16>(d, stream)
-                    : run<TN, TM, WAVES_N, WAVES_M, SWIGLU, false, bf16>(d, stream);
-    return bias ? run<TN, TM, WAVES_N, WAVES_M, SWIGLU, true, float>(d, stream)
-                : run<TN, TM, WAVES_N, WAVES_M, SWIGLU, false, float>(d, stream);
+    const bool ktail = d.K % BK != 0;
+    if (bias)
+        return ktail ? run_out<TN, TM, WAVES_N, WAVES_M, SWIGLU, true, true>(d, stream)
+                     : run_out<TN, TM, WAVES_N, WAVES_M, SWIGLU, true, false>(d, stream);
+    return ktail ? run_out<TN, TM, WAVES_N, WAVES_M, SWIGLU, false, true>(d, stream)
+                 : run_out<TN, TM, WAVES_N, WAVES_M, SWIGLU, false, false>(d, stream);
 }
 
 }  // namespace
 
 tp_status_t launch_gemm(const LinearDesc& d, hipStream_t stream) {
+    // Byte offsets inside an operand are 32-bit.
+    if ((int64_t)d.N * d.K * 2 >= (int64_t(1) << 32) || (int64_t)d.M * d.ldx * 2 >= (int64_t(1) << 32))
+        return TP_ERR_SHAPE;
     int cus = 256;
     {
         int dev = 0, n = 0;
@@ -231,15 +502,21 @@ tp_status_t launch_gemm(const LinearDesc& d, hipStream_t stream) {
             hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
             cus = n;
     }
-    // Large tiles (256 x 256, one workgroup per CU) when they fill the chip, else
-    // 128 x 128 tiles (two workgroups per CU).
+    // 256 x 256 tiles (4 waves of 128 x 128, one workgroup per CU) when they fill the
+    // chip, else 128 x 128 tiles (4 waves of 64 x 64, two workgroups per CU).
+    // Large tiles use the LDS-DMA kernel when K is a whole number of 32-wide slices.
+    const bool dma = d.K % DBK == 0;
     if (d.swiglu) {
         const int64_t big = ceil_div(d.N, 128) * ceil_div(d.M, 256);
-        if (big >= cus) return run_bias<128, 256, 2, 4, true>(d, stream);
+        if (big >= cus)
+            return dma ? run_dtl_bias<128, 256, 2, TP_DMA_WAVES_M, true>(d, stream)
+                       : run_bias<128, 256, 2, 2, true>(d, stream);
         return run_bias<64, 128, 2, 2, true>(d, stream);
     }
     const int64_t big = ceil_div(d.N, 256) * ceil_div(d.M, 256);
-    if (big >= cus) return run_bias<256, 256, 2, 4, false>(d, stream);
+    if (big >= cus)
+        return dma ? run_dtl_bias<256, 256, 2, TP_DMA_WAVES_M, false>(d, stream)
+                   : run_bias<256, 256, 2, 2, false>(d, stream);
     return run_bias<128, 128, 2, 2, false>(d, stream);
 }
 

@@ -273,11 +273,13 @@ tp_status_t tp_release_workspaces(void) {
     for (auto& kv : g_ws) {
         if (kv.second.base) {
             int prev = 0;
-            hipGetDevice(&prev);
-            hipSetDevice(kv.first.first);
+            if (hipGetDevice(&prev) != hipSuccess || hipSetDevice(kv.first.first) != hipSuccess) {
+                st = TP_ERR_HIP;
+                continue;
+            }
             if (hipStreamSynchronize(kv.first.second) != hipSuccess || hipFree(kv.second.base) != hipSuccess)
                 st = TP_ERR_HIP;
-            hipSetDevice(prev);
+            if (hipSetDevice(prev) != hipSuccess) st = TP_ERR_HIP;
         }
     }
     g_ws.clear();
