@@ -224,33 +224,38 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_kernel(GemmParams p) {
 //
 // gfx950's global_load_lds_dwordx4 writes each lane's 16 bytes straight into LDS
 // (at a wave-uniform LDS address + 16 * lane), so staging needs no registers and
-// the LDS ring can hold four 32-wide K slices: three are in flight while the
-// matrix cores consume the fourth (a fifth slice, all 160 KB, measured no faster). Holding more than one slice in registers
-// would not fit next to the 128 x 128 accumulator tile of each wave.
+// the LDS ring can hold several BK-wide K slices while the matrix cores consume
+// one. Holding more than one slice in registers would not fit next to the
+// 128 x 128 accumulator tile of each wave.
 //
-// LDS row = 32 bf16 = 64 bytes = 4 chunks of 16 bytes; chunk c of row r is stored
-// at position c ^ ((r >> 2) & 3). A DMA instruction fills 16 consecutive rows
-// (1 KB, 4 lanes per row, each lane fetching the chunk that belongs at its
-// position), and an MFMA operand read (16 lanes = 16 consecutive rows, one chunk)
-// touches 16 distinct 16-byte bank groups.
+// LDS row = BK bf16 = CPR chunks of 16 bytes. gfx950 serves a 16-byte-per-lane
+// LDS access 16 lanes (256 bytes, 64 banks) at a time; chunk c of row r is stored
+// at position c ^ ((r / RPW) % CPR), RPW = rows per 256-byte window, so the 16
+// rows read by an MFMA operand access (one chunk each) hit 16 distinct 16-byte
+// bank groups. A DMA instruction fills 64 / CPR consecutive rows (1 KB), each lane
+// fetching the chunk that belongs at its position.
 //
-// Synchronisation is explicit: before slice k is read, each wave waits until its
-// own DMA for slice k has landed (vmcnt, loads complete in order), then all waves
-// meet at s_barrier; only then is slice k+3 requested into the buffer that held
-// slice k-1, which every wave has finished reading.
+// Synchronisation is explicit: before slice k+1 is read, each wave has drained its
+// LDS reads of slice k and waited until its own DMA for slice k+1 has landed
+// (vmcnt: DMA completes in order), and all waves meet at s_barrier. Only then is
+// slice k + STAGES requested, into slice k's buffer.
 // ---------------------------------------------------------------------------------
-constexpr int DBK = 32;      // K slice per stage
+#ifndef TP_DMA_BK
+#define TP_DMA_BK 64
+#endif
 #ifndef TP_DMA_STAGES
-#define TP_DMA_STAGES 4
+#define TP_DMA_STAGES 2
 #endif
 #ifndef TP_DMA_WAVES_M
 #define TP_DMA_WAVES_M 2
 #endif
-constexpr int DSTAGES = TP_DMA_STAGES;  // LDS ring depth (4 x 32 KB)
+constexpr int DBK = TP_DMA_BK;          // K slice per stage
+constexpr int DSTAGES = TP_DMA_STAGES;  // LDS ring depth
 
 constexpr unsigned vmcnt_wait(int n) {  // s_waitcnt immediate: vmcnt(n), no other wait
     return (unsigned)((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
+constexpr unsigned kLgkm0 = 0xC07F;     // s_waitcnt immediate: lgkmcnt(0) only
 
 __device__ __forceinline__ void dma16(const char* g, char* l) {
     __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(g), (__attribute__((address_space(3))) void*)l, 16,
@@ -265,12 +270,19 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void gemm_dtl_kernel(GemmPar
     constexpr int NA = SWIGLU ? 2 * BN : BN;
     constexpr int WROWS = SWIGLU ? 2 * TN : TN;
     constexpr int ROWS = WROWS + TM;
-    constexpr int ROWB = DBK * 2;              // bytes per LDS row
+    constexpr int ROWB = DBK * 2;             // bytes per LDS row
+    constexpr int CPR = DBK / 8;              // 16-byte chunks per row
+    constexpr int RPW = 256 / ROWB;           // rows per 256-byte bank window
+    constexpr int RPI = 64 / CPR;             // rows per DMA instruction
     constexpr int STAGEB = ROWS * ROWB;
-    constexpr int IPW = ROWS / 16 / NWAVES;    // DMA instructions per wave per stage
+    constexpr int IPW = ROWS / RPI / NWAVES;  // DMA instructions per wave per stage
+    constexpr int KS = DBK / 16;              // MFMA sub-steps per slice
+    static_assert(DBK == 32 || DBK == 64, "slice width");
+    static_assert(KS % 2 == 0, "sub-steps alternate between two fragment sets");
     static_assert(WN % 32 == 0 && WM % 32 == 0, "wave tile must be whole 32x32 blocks");
-    static_assert(ROWS % 64 == 0 && (IPW * 16) % 16 == 0, "each wave fills whole 16-row groups");
-    static_assert((TN % (IPW * 16)) == 0 && (WROWS % (IPW * 16)) == 0, "a wave's rows come from one operand");
+    static_assert(ROWS % (RPI * NWAVES) == 0, "each wave fills whole DMA row groups");
+    static_assert(TN % (IPW * RPI) == 0 && WROWS % (IPW * RPI) == 0, "a wave's rows come from one operand");
+    static_assert(32 % (RPW * CPR) == 0, "swizzle period divides a 32-row block");
 
     __shared__ __attribute__((aligned(1024))) char lds[DSTAGES][STAGEB];
 
@@ -284,8 +296,8 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void gemm_dtl_kernel(GemmPar
     tile_of(blockIdx.x, p.tiles_n, p.tiles_m, tn, tm);
     const int n0 = tn * TN, m0 = tm * TM;
 
-    // This wave's DMA rows: (wave * IPW + j) * 16 + lane / 4, all from one operand.
-    const int wrow0 = wave * IPW * 16;
+    // This wave's DMA rows: wrow0 + j * RPI + lane / CPR, all from one operand.
+    const int wrow0 = wave * IPW * RPI;
     const char* gbase;
     if (wrow0 < WROWS) {
         const bool up = SWIGLU && wrow0 >= TN;
@@ -296,8 +308,8 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void gemm_dtl_kernel(GemmPar
     uint32_t goff[IPW];
 #pragma unroll
     for (int j = 0; j < IPW; ++j) {
-        const int row = wrow0 + j * 16 + (lane >> 2);
-        const int c = (lane & 3) ^ ((row >> 2) & 3);  // the chunk that belongs at this lane's position
+        const int row = wrow0 + j * RPI + lane / CPR;
+        const int c = (lane % CPR) ^ ((row / RPW) % CPR);  // the chunk that belongs at this lane's position
         if (wrow0 < WROWS) {
             const bool up = SWIGLU && row >= TN;
             const int n = min(n0 + (up ? row - TN : row), p.N - 1);
@@ -324,8 +336,8 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void gemm_dtl_kernel(GemmPar
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
     // Operand reads: every block starts on a multiple of 32 rows, so this lane's
-    // swizzle term is (l32 >> 2) & 3 for all of them.
-    const int sw = (l32 >> 2) & 3;
+    // swizzle term is (l32 / RPW) % CPR for all of them.
+    const int sw = (l32 / RPW) % CPR;
     int arow[NA];
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
@@ -347,12 +359,12 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void gemm_dtl_kernel(GemmPar
             for (int j = 0; j < BM; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     };
-
-    // Wait until this wave's DMA for slice k has landed (DMA completes in order; `ahead`
-    // slices were requested after it), then meet the other waves.
+    // Wait until this wave's DMA for the next slice has landed (`ahead` slices were
+    // requested after it), then meet the other waves.
     auto sync_slice = [&](int ahead) {
-        static_assert(DSTAGES <= 5, "waits below cover up to 3 slices ahead");
-        if (ahead >= 3) __builtin_amdgcn_s_waitcnt(vmcnt_wait(3 * IPW));
+        static_assert(DSTAGES <= 5, "waits below cover up to 4 slices ahead");
+        if (ahead >= 4) __builtin_amdgcn_s_waitcnt(vmcnt_wait(4 * IPW));
+        else if (ahead == 3) __builtin_amdgcn_s_waitcnt(vmcnt_wait(3 * IPW));
         else if (ahead == 2) __builtin_amdgcn_s_waitcnt(vmcnt_wait(2 * IPW));
         else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vmcnt_wait(IPW));
         else __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));  // also for a slice past the end
@@ -361,36 +373,39 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void gemm_dtl_kernel(GemmPar
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
     };
 
-    // Prologue: slices 0 .. DSTAGES-2 requested; sub-step 0 of slice 0 read.
-    for (int s = 0; s < DSTAGES - 1 && s < KT; ++s) issue_stage(s, s);
-    sync_slice(min(KT - 1, DSTAGES - 2));
+    // Prologue: every buffer requested; sub-step 0 of slice 0 read.
+    for (int s = 0; s < DSTAGES && s < KT; ++s) issue_stage(s, s);
+    sync_slice(min(KT - 1, DSTAGES - 1));
     bf16x8 fa0[NA], fb0[BM], fa1[NA], fb1[BM];
     read_frags(lds[0], 0, fa0, fb0);
-    // Nothing but these LDS reads may be pending on lgkmcnt when the loop starts, so
-    // the waits inside it can count in-order LDS returns.
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    // Per slice k: read sub-step 1 | MFMAs of sub-step 0 | barrier for slice k+1 and
-    // request slice k+DSTAGES-1 into slice k-1's buffer | read sub-step 0 of slice k+1 |
-    // MFMAs of sub-step 1. Every LDS read has one MFMA phase to land.
-    // lgkmcnt has 4 bits: with two batches of 8 reads outstanding the compiler could
+    // lgkmcnt has 4 bits: with two batches of reads outstanding the compiler could
     // only wait for zero. Each batch is therefore drained (it had a whole MFMA phase
     // to land, so this does not stall) before the next one is issued.
+    __builtin_amdgcn_s_waitcnt(kLgkm0);
+    // Per sub-step: request the next fragments, run this sub-step's MFMAs. Before the
+    // last sub-step of slice k, synchronise on slice k+1 and refill slice k's buffer.
     for (int kt = 0; kt < KT; ++kt) {
         const char* s = lds[kt % DSTAGES];
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): sub-step 0 of slice k is in
-        read_frags(s, 1, fa1, fb1);
-        __builtin_amdgcn_sched_barrier(0);
-        mfmas(fa0, fb0);
-        __builtin_amdgcn_sched_barrier(0);
-        // Unconditional, so every path into the MFMAs below is the same. On the last
-        // slice this synchronises once more and reads a buffer nobody uses any more.
-        sync_slice(min(KT - 2 - kt, DSTAGES - 3));
-        if (kt + DSTAGES - 1 < KT) issue_stage(kt + DSTAGES - 1, (kt + DSTAGES - 1) % DSTAGES);
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): sub-step 1 of slice k is in
-        read_frags(lds[(kt + 1) % DSTAGES], 0, fa0, fb0);
-        __builtin_amdgcn_sched_barrier(0);
-        mfmas(fa1, fb1);
-        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bool even = (ks & 1) == 0;
+            if (ks + 1 < KS) {
+                if (even) read_frags(s, ks + 1, fa1, fb1);
+                else read_frags(s, ks + 1, fa0, fb0);
+            } else {
+                // Unconditional, so every path into the MFMAs below is the same. On
+                // the last slice this synchronises once more and reads a buffer
+                // nobody uses any more.
+                sync_slice(min(KT - 2 - kt, DSTAGES - 2));
+                if (kt + DSTAGES < KT) issue_stage(kt + DSTAGES, kt % DSTAGES);
+                read_frags(lds[(kt + 1) % DSTAGES], 0, fa0, fb0);  // KS is even: the next set is fa0
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (even) mfmas(fa0, fb0);
+            else mfmas(fa1, fb1);
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt(kLgkm0);
+        }
     }
 
 #pragma unroll
@@ -504,7 +519,7 @@ tp_status_t launch_gemm(const LinearDesc& d, hipStream_t stream) {
     }
     // 256 x 256 tiles (4 waves of 128 x 128, one workgroup per CU) when they fill the
     // chip, else 128 x 128 tiles (4 waves of 64 x 64, two workgroups per CU).
-    // Large tiles use the LDS-DMA kernel when K is a whole number of 32-wide slices.
+    // Large tiles use the LDS-DMA kernel when K is a whole number of slices.
     const bool dma = d.K % DBK == 0;
     if (d.swiglu) {
         const int64_t big = ceil_div(d.N, 128) * ceil_div(d.M, 256);
