@@ -25,6 +25,13 @@
 
 #include "tp_epilogue.h"
 
+#ifndef TP_SKINNY_WG_PER_CU
+#define TP_SKINNY_WG_PER_CU 1
+#endif
+#ifndef TP_SKINNY_U1
+#define TP_SKINNY_U1 4
+#endif
+
 namespace tp {
 namespace {
 
@@ -259,10 +266,11 @@ tp_status_t run(const LinearDesc& d, hipStream_t stream) {
     p.N = (int)d.N;
     p.K = (int)d.K;
 
-    // Work decomposition: G row groups of 16*RH outputs; split K across workgroups
-    // only as far as needed to give every CU about two workgroups.
+    // Work decomposition: G row groups of 16*RH outputs. K is split across
+    // workgroups only when there are fewer row groups than CUs (measured: longer
+    // per-wave streams beat a second workgroup per CU once every CU has one).
     const int64_t G = ceil_div(d.N, 16 * RH);
-    const int64_t target = 2 * (int64_t)device_cus();
+    const int64_t target = TP_SKINNY_WG_PER_CU * (int64_t)device_cus();
     int64_t S = ceil_div(target, G);
     const int64_t smax = std::max<int64_t>(1, d.K / (NW * KS));
     S = std::min<int64_t>(std::max<int64_t>(S, 1), std::min<int64_t>(smax, 64));
@@ -300,7 +308,7 @@ tp_status_t launch_skinny(const LinearDesc& d, hipStream_t stream) {
     const int mt = (int)ceil_div(d.M, 16);
     if (d.swiglu) {
         switch (mt) {
-            case 1: return run_bias<1, 2, 8, 4, true>(d, stream);
+            case 1: return run_bias<1, 2, 8, TP_SKINNY_U1, true>(d, stream);
             case 2: return run_bias<2, 2, 4, 2, true>(d, stream);
             case 3: return run_bias<3, 2, 4, 2, true>(d, stream);
             case 4: return run_bias<4, 4, 4, 1, true>(d, stream);
@@ -308,7 +316,7 @@ tp_status_t launch_skinny(const LinearDesc& d, hipStream_t stream) {
         }
     }
     switch (mt) {
-        case 1: return run_bias<1, 1, 8, 4, false>(d, stream);
+        case 1: return run_bias<1, 1, 8, TP_SKINNY_U1, false>(d, stream);
         case 2: return run_bias<2, 2, 4, 2, false>(d, stream);
         case 3: return run_bias<3, 2, 4, 2, false>(d, stream);
         case 4: return run_bias<4, 4, 4, 1, false>(d, stream);
