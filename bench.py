@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time")
+    ap.add_argument("--traffic-copy-mib", type=int, default=0,
+                    help="first run one plain contiguous copy of this many MiB (counter calibration)")
     return ap.parse_args()
 
 
@@ -281,6 +283,17 @@ def main():
     import torch
     import tp_inputs as I
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.traffic_copy_mib > 0:
+        # A plain copy of known size: reads and writes exactly n bytes each. Under
+        # rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE it calibrates the counters.
+        import tensor_transformer_linear_col_amd as tp
+        cols = 8192
+        rows = args.traffic_copy_mib * (1 << 20) // (2 * cols)
+        src = torch.ones(rows, cols, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        tp.tp_shard_weight(src, rows, cols, 1, 0, 0, dst)
+        torch.cuda.synchronize()
+        del src, dst
     shape = I.LLAMA70B_LAYER_TP8
     layer = Layer(shape)
 
