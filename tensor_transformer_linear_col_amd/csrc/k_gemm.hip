@@ -222,8 +222,8 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_kernel(GemmParams p) {
 // ---------------------------------------------------------------------------------
 // Large-tile kernel with direct global -> LDS loads.
 //
-// gfx950's global_load_lds_dwordx4 writes each lane's 16 bytes straight into LDS
-// (at a wave-uniform LDS address + 16 * lane), so staging needs no registers and
+// gfx950's buffer_load_dwordx4 ... lds writes each lane's 16 bytes straight into
+// LDS (at a wave-uniform LDS address + 16 * lane), so staging needs no registers and
 // the LDS ring can hold several BK-wide K slices while the matrix cores consume
 // one. Holding more than one slice in registers would not fit next to the
 // 128 x 128 accumulator tile of each wave.
@@ -257,9 +257,21 @@ constexpr unsigned vmcnt_wait(int n) {  // s_waitcnt immediate: vmcnt(n), no oth
 }
 constexpr unsigned kLgkm0 = 0xC07F;     // s_waitcnt immediate: lgkmcnt(0) only
 
-__device__ __forceinline__ void dma16(const char* g, char* l) {
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(g), (__attribute__((address_space(3))) void*)l, 16,
-                                     0, 0);
+// One wave's DMA of a stage: IPW instructions of 1 KB each into consecutive LDS
+// blocks, through a raw buffer descriptor of the operand (bounds = its byte size).
+// The descriptor type exists only for the GPU target, so the body is compiled in
+// the device pass alone (the host pass only needs the kernel's launch stub).
+template <int IPW>
+__device__ __forceinline__ void dma_rows(const void* base, uint32_t bytes, const uint32_t (&goff)[IPW], uint32_t koff,
+                                         char* l) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+#pragma unroll
+    for (int j = 0; j < IPW; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(l + j * 1024), 16,
+                                                 goff[j], koff, 0, 0);
+#endif
 }
 
 template <int TN, int TM, int WAVES_N, int WAVES_M, bool SWIGLU, bool BIAS, typename OutT>
@@ -288,7 +300,10 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void gemm_dtl_kernel(GemmPar
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // The wave index is uniform; saying so keeps the DMA base address and the LDS
+    // destination (M0) in scalar registers, so each DMA is one instruction with a
+    // 32-bit per-lane offset instead of a 64-bit vector address computation.
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wn = wave % WAVES_N, wm = wave / WAVES_N;
     const int l32 = lane & 31, lh = lane >> 5;
 
@@ -296,21 +311,20 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void gemm_dtl_kernel(GemmPar
     tile_of(blockIdx.x, p.tiles_n, p.tiles_m, tn, tm);
     const int n0 = tn * TN, m0 = tm * TM;
 
-    // This wave's DMA rows: wrow0 + j * RPI + lane / CPR, all from one operand.
+    // This wave's DMA rows: wrow0 + j * RPI + lane / CPR, all from one operand, read
+    // through a buffer descriptor of that operand (scalar base and size, 32-bit
+    // per-lane offsets, the K slice's offset as the scalar offset).
     const int wrow0 = wave * IPW * RPI;
-    const char* gbase;
-    if (wrow0 < WROWS) {
-        const bool up = SWIGLU && wrow0 >= TN;
-        gbase = reinterpret_cast<const char*>(up ? p.W1 : p.W0);
-    } else {
-        gbase = reinterpret_cast<const char*>(p.X);
-    }
+    const bool wop = wrow0 < WROWS;
+    const bool wup = SWIGLU && wop && wrow0 >= TN;
+    const void* obase = wop ? (wup ? (const void*)p.W1 : (const void*)p.W0) : (const void*)p.X;
+    const int64_t obytes = wop ? (int64_t)p.N * p.K * 2 : (int64_t)(p.M - 1) * p.ldx * 2 + (int64_t)p.K * 2;
     uint32_t goff[IPW];
 #pragma unroll
     for (int j = 0; j < IPW; ++j) {
         const int row = wrow0 + j * RPI + lane / CPR;
         const int c = (lane % CPR) ^ ((row / RPW) % CPR);  // the chunk that belongs at this lane's position
-        if (wrow0 < WROWS) {
+        if (wop) {
             const bool up = SWIGLU && row >= TN;
             const int n = min(n0 + (up ? row - TN : row), p.N - 1);
             goff[j] = (uint32_t)(((int64_t)n * p.K + c * 8) * 2);
@@ -321,10 +335,7 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void gemm_dtl_kernel(GemmPar
     }
     const int KT = p.K / DBK;
     auto issue_stage = [&](int kt, int buf) {
-        const char* g = gbase + (int64_t)kt * DBK * 2;
-        char* l = &lds[buf][wrow0 * ROWB];
-#pragma unroll
-        for (int j = 0; j < IPW; ++j) dma16(g + goff[j], l + j * 1024);
+        dma_rows<IPW>(obase, (uint32_t)obytes, goff, (uint32_t)(kt * DBK * 2), &lds[buf][wrow0 * ROWB]);
     };
 
     floatx16 acc[NA][BM];
