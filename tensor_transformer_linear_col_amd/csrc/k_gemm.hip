@@ -249,6 +249,9 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_kernel(GemmParams p) {
 #ifndef TP_DMA_WAVES_M
 #define TP_DMA_WAVES_M 2
 #endif
+#ifndef TP_DMA_SPREAD
+#define TP_DMA_SPREAD 2
+#endif
 constexpr int DBK = TP_DMA_BK;          // K slice per stage
 constexpr int DSTAGES = TP_DMA_STAGES;  // LDS ring depth
 
@@ -261,14 +264,14 @@ constexpr unsigned kLgkm0 = 0xC07F;     // s_waitcnt immediate: lgkmcnt(0) only
 // blocks, through a raw buffer descriptor of the operand (bounds = its byte size).
 // The descriptor type exists only for the GPU target, so the body is compiled in
 // the device pass alone (the host pass only needs the kernel's launch stub).
-template <int IPW>
+template <int IPW, int J0 = 0, int J1 = IPW>
 __device__ __forceinline__ void dma_rows(const void* base, uint32_t bytes, const uint32_t (&goff)[IPW], uint32_t koff,
                                          char* l) {
 #if defined(__HIP_DEVICE_COMPILE__)
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 #pragma unroll
-    for (int j = 0; j < IPW; ++j)
+    for (int j = J0; j < J1; ++j)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(l + j * 1024), 16,
                                                  goff[j], koff, 0, 0);
 #endif
@@ -394,9 +397,20 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void gemm_dtl_kernel(GemmPar
     // to land, so this does not stall) before the next one is issued.
     __builtin_amdgcn_s_waitcnt(kLgkm0);
     // Per sub-step: request the next fragments, run this sub-step's MFMAs. Before the
-    // last sub-step of slice k, synchronise on slice k+1 and refill slice k's buffer.
+    // last sub-step of slice k, synchronise on slice k+1. The buffer slice k-1 left
+    // free is refilled (with slice k-1+STAGES) during the first NSPREAD sub-steps of
+    // slice k, one DMA after each MFMA, so issuing them does not idle the matrix
+    // cores. With NSPREAD = 0 the refill is issued right after the barrier.
+    constexpr int NSPREAD = TP_DMA_SPREAD;
+    static_assert(NSPREAD >= 0 && NSPREAD <= KS && (NSPREAD == 0 || IPW % NSPREAD == 0), "DMA spread");
+    constexpr int DPS = NSPREAD ? IPW / NSPREAD : IPW;  // DMA instructions per spread sub-step
+    static_assert(NSPREAD == 0 || DPS <= NA * BM, "one DMA per MFMA at most");
     for (int kt = 0; kt < KT; ++kt) {
         const char* s = lds[kt % DSTAGES];
+        const int refill = kt - 1 + DSTAGES;
+        const bool do_refill = NSPREAD > 0 && kt >= 1 && refill < KT;
+        const uint32_t rkoff = (uint32_t)(refill * DBK * 2);
+        char* rl = &lds[(kt + DSTAGES - 1) % DSTAGES][wrow0 * ROWB];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const bool even = (ks & 1) == 0;
@@ -408,12 +422,28 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void gemm_dtl_kernel(GemmPar
                 // the last slice this synchronises once more and reads a buffer
                 // nobody uses any more.
                 sync_slice(min(KT - 2 - kt, DSTAGES - 2));
-                if (kt + DSTAGES < KT) issue_stage(kt + DSTAGES, kt % DSTAGES);
+                if (NSPREAD == 0 && kt + DSTAGES < KT) issue_stage(kt + DSTAGES, kt % DSTAGES);
                 read_frags(lds[(kt + 1) % DSTAGES], 0, fa0, fb0);  // KS is even: the next set is fa0
             }
             __builtin_amdgcn_sched_barrier(0);
-            if (even) mfmas(fa0, fb0);
-            else mfmas(fa1, fb1);
+            if (ks < NSPREAD) {
+                // Uniform branch; the DMA of this part goes between the MFMAs.
+                if (do_refill) {
+                    if (ks == 0) dma_rows<IPW, 0, DPS>(obase, (uint32_t)obytes, goff, rkoff, rl);
+                    else if (ks == 1 && NSPREAD > 1) dma_rows<IPW, (NSPREAD > 1 ? DPS : 0), (NSPREAD > 1 ? 2 * DPS : 0)>(obase, (uint32_t)obytes, goff, rkoff, rl);
+                }
+                if (even) mfmas(fa0, fb0);
+                else mfmas(fa1, fb1);
+#pragma unroll
+                for (int q = 0; q < DPS; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one VMEM read (a DMA)
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, NA * BM - DPS, 0);
+            } else {
+                if (even) mfmas(fa0, fb0);
+                else mfmas(fa1, fb1);
+            }
             __builtin_amdgcn_sched_barrier(0);
             __builtin_amdgcn_s_waitcnt(kLgkm0);
         }

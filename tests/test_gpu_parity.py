@@ -324,3 +324,46 @@ def test_errors_raise_before_launch():
     with pytest.raises(tp.TPError) as e:
         tp.tp_linear_col(X, W, None, Y, 2, 4096, 11008, 3)
     assert e.value.status == 3
+
+
+# ---- the large-tile LDS-DMA kernel: ragged token and feature tails ------------------------
+# It runs when 256 x 256 tiles (128 x 256 for SwiGLU) alone fill the chip and K is a
+# multiple of 64, so these shapes are large; the oracle checks sampled token rows.
+
+DMA_SHAPES = [  # (M, K, N): tails in M and N, K a multiple of 64
+    (2100, 1024, 8168), (4096 + 33, 576, 8192 - 40), (8192, 128, 8192 + 8),
+]
+
+
+def _sample_rows(M):
+    rng = np.random.default_rng(M)
+    return np.unique(np.concatenate([[0, M - 1], rng.choice(M, 6, replace=False)]))
+
+
+@pytest.mark.parametrize("M,K,N", DMA_SHAPES)
+def test_dma_kernel_tails(M, K, N):
+    log_case("dma kernel tails", M, K, N)
+    x, w, b = I.activations(M, K, 301), I.weight(N, K, 302), I.bias(N, 303)
+    buf, Y = canary_buffer((M, N), torch.bfloat16)
+    tp.tp_linear_col(dev(x), dev(w), dev(b), Y, M, K, N, 1)
+    torch.cuda.synchronize()
+    rows = _sample_rows(M)
+    ref = O.linear(host64(x)[rows], host64(w), host64(b))
+    assert err(Y.cpu()[rows], ref) <= BF16_TOL
+    assert canaries_intact(buf, (M, N))
+
+
+@pytest.mark.parametrize("M,K,I_", [(2310, 512, 3584 - 24), (4096, 64, 4096 + 40)])
+def test_dma_kernel_swiglu_tails(M, K, I_):
+    log_case("dma kernel swiglu tails", M, K, I_)
+    x = I.activations(M, K, 311)
+    wg, wu = I.weight(I_, K, 312), I.weight(I_, K, 313)
+    bg, bu = I.bias(I_, 314), I.bias(I_, 315)
+    buf, H = canary_buffer((M, I_), torch.bfloat16)
+    tp.tp_mlp_shard(dev(x), dev(wg), dev(wu), dev(bg), dev(bu), None, H, None, M, K, I_, 1)
+    torch.cuda.synchronize()
+    rows = _sample_rows(M)
+    xs = host64(x)[rows]
+    ref = O.swiglu(O.linear(xs, host64(wg), host64(bg)), O.linear(xs, host64(wu), host64(bu)))
+    assert err(H.cpu()[rows], ref) <= BF16_TOL
+    assert canaries_intact(buf, (M, I_))
