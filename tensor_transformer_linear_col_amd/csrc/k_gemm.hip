@@ -24,6 +24,8 @@
 // MFMA 32x32x16 operand mapping (lane l, l32 = l % 32, lh = l / 32):
 //   A: lane l holds W[n0 + l32][k0 + 8*lh .. +7];  B: lane l holds X[m0 + l32][k0 + 8*lh .. +7]
 //   D: register e of lane l holds D[n0 + 8*(e/4) + 4*lh + e%4][m0 + l32]
+#include <type_traits>
+
 #include "tp_epilogue.h"
 
 namespace tp {
@@ -264,16 +266,19 @@ constexpr unsigned kLgkm0 = 0xC07F;     // s_waitcnt immediate: lgkmcnt(0) only
 // blocks, through a raw buffer descriptor of the operand (bounds = its byte size).
 // The descriptor type exists only for the GPU target, so the body is compiled in
 // the device pass alone (the host pass only needs the kernel's launch stub).
-template <int IPW, int J0 = 0, int J1 = IPW>
+// Instructions j0 <= j < j1 only; callers pass bounds that are constants once their
+// loops are unrolled, so the selection costs nothing.
+template <int IPW>
 __device__ __forceinline__ void dma_rows(const void* base, uint32_t bytes, const uint32_t (&goff)[IPW], uint32_t koff,
-                                         char* l) {
+                                         char* l, int j0 = 0, int j1 = IPW) {
 #if defined(__HIP_DEVICE_COMPILE__)
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 #pragma unroll
-    for (int j = J0; j < J1; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(l + j * 1024), 16,
-                                                 goff[j], koff, 0, 0);
+    for (int j = 0; j < IPW; ++j)
+        if (j >= j0 && j < j1)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(l + j * 1024), 16,
+                                                     goff[j], koff, 0, 0);
 #endif
 }
 
@@ -396,58 +401,57 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void gemm_dtl_kernel(GemmPar
     // only wait for zero. Each batch is therefore drained (it had a whole MFMA phase
     // to land, so this does not stall) before the next one is issued.
     __builtin_amdgcn_s_waitcnt(kLgkm0);
-    // Per sub-step: request the next fragments, run this sub-step's MFMAs. Before the
-    // last sub-step of slice k, synchronise on slice k+1. The buffer slice k-1 left
-    // free is refilled (with slice k-1+STAGES) during the first NSPREAD sub-steps of
-    // slice k, one DMA after each MFMA, so issuing them does not idle the matrix
-    // cores. With NSPREAD = 0 the refill is issued right after the barrier.
+    // Per sub-step: request the next fragments and run this sub-step's MFMAs, each
+    // fragment read issued right behind an MFMA so the matrix cores never wait on the
+    // LDS queue. Before the last sub-step of slice k, synchronise on slice k+1. The
+    // buffer slice k-1 left free is refilled (with slice k-1+STAGES) during the first
+    // NSPREAD sub-steps of slice k, one DMA behind every few MFMAs. Whether a slice
+    // refills is a template flag, so no branch splits a sub-step and the interleaving
+    // below holds for every slice.
     constexpr int NSPREAD = TP_DMA_SPREAD;
-    static_assert(NSPREAD >= 0 && NSPREAD <= KS && (NSPREAD == 0 || IPW % NSPREAD == 0), "DMA spread");
-    constexpr int DPS = NSPREAD ? IPW / NSPREAD : IPW;  // DMA instructions per spread sub-step
-    static_assert(NSPREAD == 0 || DPS <= NA * BM, "one DMA per MFMA at most");
-    for (int kt = 0; kt < KT; ++kt) {
+    static_assert(NSPREAD >= 1 && NSPREAD <= KS && IPW % NSPREAD == 0, "DMA spread");
+    constexpr int NMF = NA * BM;                 // MFMAs per sub-step
+    constexpr int NRD = NA + BM;                 // fragment reads per sub-step
+    constexpr int DPS = IPW / NSPREAD;           // DMA instructions per spread sub-step
+    static_assert(NRD + DPS <= NMF, "one fragment read or DMA per MFMA");
+    auto slice = [&](int kt, auto refill_tag) {
+        constexpr bool REFILL = decltype(refill_tag)::value;
         const char* s = lds[kt % DSTAGES];
-        const int refill = kt - 1 + DSTAGES;
-        const bool do_refill = NSPREAD > 0 && kt >= 1 && refill < KT;
-        const uint32_t rkoff = (uint32_t)(refill * DBK * 2);
+        const uint32_t rkoff = (uint32_t)((kt - 1 + DSTAGES) * DBK * 2);
         char* rl = &lds[(kt + DSTAGES - 1) % DSTAGES][wrow0 * ROWB];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const bool even = (ks & 1) == 0;
-            if (ks + 1 < KS) {
-                if (even) read_frags(s, ks + 1, fa1, fb1);
-                else read_frags(s, ks + 1, fa0, fb0);
-            } else {
-                // Unconditional, so every path into the MFMAs below is the same. On
-                // the last slice this synchronises once more and reads a buffer
-                // nobody uses any more.
+            if (ks + 1 == KS) {
+                // On the last slice this synchronises once more and reads a buffer
+                // nobody uses any more, so every slice takes the same path.
                 sync_slice(min(KT - 2 - kt, DSTAGES - 2));
-                if (NSPREAD == 0 && kt + DSTAGES < KT) issue_stage(kt + DSTAGES, kt % DSTAGES);
-                read_frags(lds[(kt + 1) % DSTAGES], 0, fa0, fb0);  // KS is even: the next set is fa0
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
-            if (ks < NSPREAD) {
-                // Uniform branch; the DMA of this part goes between the MFMAs.
-                if (do_refill) {
-                    if (ks == 0) dma_rows<IPW, 0, DPS>(obase, (uint32_t)obytes, goff, rkoff, rl);
-                    else if (ks == 1 && NSPREAD > 1) dma_rows<IPW, (NSPREAD > 1 ? DPS : 0), (NSPREAD > 1 ? 2 * DPS : 0)>(obase, (uint32_t)obytes, goff, rkoff, rl);
-                }
-                if (even) mfmas(fa0, fb0);
-                else mfmas(fa1, fb1);
+            const char* src = ks + 1 < KS ? s : lds[(kt + 1) % DSTAGES];
+            const int nks = ks + 1 < KS ? ks + 1 : 0;
+            if (even) read_frags(src, nks, fa1, fb1);  // KS is even: sets alternate 0, 1, 0, 1
+            else read_frags(src, nks, fa0, fb0);
+            if (REFILL && ks < NSPREAD) dma_rows<IPW>(obase, (uint32_t)obytes, goff, rkoff, rl, ks * DPS, (ks + 1) * DPS);
+            if (even) mfmas(fa0, fb0);
+            else mfmas(fa1, fb1);
+            // The DMAs write LDS, so the compiler keeps every fragment read ahead of
+            // them: reads go behind the first MFMAs, DMAs behind the following ones.
 #pragma unroll
-                for (int q = 0; q < DPS; ++q) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one VMEM read (a DMA)
-                }
-                __builtin_amdgcn_sched_group_barrier(0x008, NA * BM - DPS, 0);
-            } else {
-                if (even) mfmas(fa0, fb0);
-                else mfmas(fa1, fb1);
+            for (int q = 0; q < NMF; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                if (q < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+                else if (REFILL && ks < NSPREAD && q - NRD < DPS)
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one DMA
             }
             __builtin_amdgcn_sched_barrier(0);
             __builtin_amdgcn_s_waitcnt(kLgkm0);
         }
-    }
+    };
+    slice(0, std::false_type{});  // the prologue filled every buffer
+    int kt = 1;
+    for (; kt + DSTAGES - 1 < KT; ++kt) slice(kt, std::true_type{});
+    for (; kt < KT; ++kt) slice(kt, std::false_type{});
 
 #pragma unroll
     for (int i = 0; i < BN; ++i)
