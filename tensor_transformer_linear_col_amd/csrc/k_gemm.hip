@@ -41,18 +41,29 @@ struct GemmParams {
     OutDesc o;
     int M, N, K;
     int tiles_n, tiles_m;
+    // Split-K remainder (LDS-DMA kernel only): the first F tiles run whole, one per
+    // workgroup; each of the remaining tiles is cut into S equal K ranges, one per
+    // workgroup, whose fp32 partials meet in ws.
+    int F, S;
+    float* ws;  // one fp32 partial tile per split workgroup
 };
 
 __device__ __forceinline__ bf16x8 ld8g(const bf16* p) {
     return *reinterpret_cast<const bf16x8*>(p);
 }
 
-// Logical tile index of workgroup b: XCD-major when the tile count allows, then
-// grouped GW weight-row tiles at a time so resident tiles share panels.
-__device__ __forceinline__ void tile_of(int b, int tiles_n, int tiles_m, int& tn, int& tm) {
-    constexpr int XCDS = 8, GW = 4;
-    const int T = tiles_n * tiles_m;
-    const int L = (T % XCDS == 0) ? (b % XCDS) * (T / XCDS) + b / XCDS : b;
+// Workgroup b's logical index: the hardware deals workgroups to the 8 XCDs in
+// turn, so logical neighbours are put on one XCD (when n divides evenly) and share
+// that XCD's L2.
+__device__ __forceinline__ int xcd_major(int b, int n) {
+    constexpr int XCDS = 8;
+    return (n % XCDS == 0) ? (b % XCDS) * (n / XCDS) + b / XCDS : b;
+}
+
+// Tile of logical index L: grouped GW weight-row tiles at a time so consecutive
+// tiles share panels.
+__device__ __forceinline__ void tile_coords(int L, int tiles_n, int tiles_m, int& tn, int& tm) {
+    constexpr int GW = 4;
     const int per_group = GW * tiles_m;
     const int grp = L / per_group;
     const int first = grp * GW;
@@ -60,6 +71,11 @@ __device__ __forceinline__ void tile_of(int b, int tiles_n, int tiles_m, int& tn
     const int rem = L - grp * per_group;
     tn = first + rem % gw;
     tm = rem / gw;
+}
+
+// Tile of workgroup b when every workgroup takes one tile.
+__device__ __forceinline__ void tile_of(int b, int tiles_n, int tiles_m, int& tn, int& tm) {
+    tile_coords(xcd_major(b, tiles_n * tiles_m), tiles_n, tiles_m, tn, tm);
 }
 
 template <int TN, int TM, int WAVES_N, int WAVES_M, bool SWIGLU, bool BIAS, bool KTAIL, typename OutT>
@@ -282,7 +298,13 @@ __device__ __forceinline__ void dma_rows(const void* base, uint32_t bytes, const
 #endif
 }
 
-template <int TN, int TM, int WAVES_N, int WAVES_M, bool SWIGLU, bool BIAS, typename OutT>
+// SK: split-K remainder. Workgroups below F take one whole tile each; the others
+// take one of the S equal K ranges of a remaining tile and leave an fp32 partial
+// tile, which splitk_reduce_kernel sums in K order and finishes.
+// Workgroups that run side by side on one XCD hold neighbouring tiles at the same K
+// range, so their panels are shared in that XCD's L2 (a stream-K split, whose
+// workgroups sit at different K offsets, forfeits that sharing).
+template <int TN, int TM, int WAVES_N, int WAVES_M, bool SWIGLU, bool BIAS, bool SK, typename OutT>
 __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void gemm_dtl_kernel(GemmParams p) {
     constexpr int NWAVES = WAVES_N * WAVES_M;
     constexpr int WN = TN / WAVES_N, WM = TM / WAVES_M;
@@ -315,10 +337,6 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void gemm_dtl_kernel(GemmPar
     const int wn = wave % WAVES_N, wm = wave / WAVES_N;
     const int l32 = lane & 31, lh = lane >> 5;
 
-    int tn, tm;
-    tile_of(blockIdx.x, p.tiles_n, p.tiles_m, tn, tm);
-    const int n0 = tn * TN, m0 = tm * TM;
-
     // This wave's DMA rows: wrow0 + j * RPI + lane / CPR, all from one operand, read
     // through a buffer descriptor of that operand (scalar base and size, 32-bit
     // per-lane offsets, the K slice's offset as the scalar offset).
@@ -328,31 +346,24 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void gemm_dtl_kernel(GemmPar
     const void* obase = wop ? (wup ? (const void*)p.W1 : (const void*)p.W0) : (const void*)p.X;
     const int64_t obytes = wop ? (int64_t)p.N * p.K * 2 : (int64_t)(p.M - 1) * p.ldx * 2 + (int64_t)p.K * 2;
     uint32_t goff[IPW];
+    auto set_rows = [&](int n0, int m0) {
 #pragma unroll
-    for (int j = 0; j < IPW; ++j) {
-        const int row = wrow0 + j * RPI + lane / CPR;
-        const int c = (lane % CPR) ^ ((row / RPW) % CPR);  // the chunk that belongs at this lane's position
-        if (wop) {
-            const bool up = SWIGLU && row >= TN;
-            const int n = min(n0 + (up ? row - TN : row), p.N - 1);
-            goff[j] = (uint32_t)(((int64_t)n * p.K + c * 8) * 2);
-        } else {
-            const int m = min(m0 + row - WROWS, p.M - 1);
-            goff[j] = (uint32_t)(((int64_t)m * p.ldx + c * 8) * 2);
+        for (int j = 0; j < IPW; ++j) {
+            const int row = wrow0 + j * RPI + lane / CPR;
+            const int c = (lane % CPR) ^ ((row / RPW) % CPR);  // the chunk that belongs at this lane's position
+            if (wop) {
+                const bool up = SWIGLU && row >= TN;
+                const int n = min(n0 + (up ? row - TN : row), p.N - 1);
+                goff[j] = (uint32_t)(((int64_t)n * p.K + c * 8) * 2);
+            } else {
+                const int m = min(m0 + row - WROWS, p.M - 1);
+                goff[j] = (uint32_t)(((int64_t)m * p.ldx + c * 8) * 2);
+            }
         }
-    }
-    const int KT = p.K / DBK;
-    auto issue_stage = [&](int kt, int buf) {
-        dma_rows<IPW>(obase, (uint32_t)obytes, goff, (uint32_t)(kt * DBK * 2), &lds[buf][wrow0 * ROWB]);
     };
+    const int KT = p.K / DBK;
 
     floatx16 acc[NA][BM];
-#pragma unroll
-    for (int i = 0; i < NA; ++i)
-#pragma unroll
-        for (int j = 0; j < BM; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
     // Operand reads: every block starts on a multiple of 32 rows, so this lane's
     // swizzle term is (l32 / RPW) % CPR for all of them.
@@ -392,15 +403,6 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void gemm_dtl_kernel(GemmPar
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
     };
 
-    // Prologue: every buffer requested; sub-step 0 of slice 0 read.
-    for (int s = 0; s < DSTAGES && s < KT; ++s) issue_stage(s, s);
-    sync_slice(min(KT - 1, DSTAGES - 1));
-    bf16x8 fa0[NA], fb0[BM], fa1[NA], fb1[BM];
-    read_frags(lds[0], 0, fa0, fb0);
-    // lgkmcnt has 4 bits: with two batches of reads outstanding the compiler could
-    // only wait for zero. Each batch is therefore drained (it had a whole MFMA phase
-    // to land, so this does not stall) before the next one is issued.
-    __builtin_amdgcn_s_waitcnt(kLgkm0);
     // Per sub-step: request the next fragments and run this sub-step's MFMAs, each
     // fragment read issued right behind an MFMA so the matrix cores never wait on the
     // LDS queue. Before the last sub-step of slice k, synchronise on slice k+1. The
@@ -414,66 +416,177 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void gemm_dtl_kernel(GemmPar
     constexpr int NRD = NA + BM;                 // fragment reads per sub-step
     constexpr int DPS = IPW / NSPREAD;           // DMA instructions per spread sub-step
     static_assert(NRD + DPS <= NMF, "one fragment read or DMA per MFMA");
-    auto slice = [&](int kt, auto refill_tag) {
-        constexpr bool REFILL = decltype(refill_tag)::value;
-        const char* s = lds[kt % DSTAGES];
-        const uint32_t rkoff = (uint32_t)((kt - 1 + DSTAGES) * DBK * 2);
-        char* rl = &lds[(kt + DSTAGES - 1) % DSTAGES][wrow0 * ROWB];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const bool even = (ks & 1) == 0;
-            if (ks + 1 == KS) {
-                // On the last slice this synchronises once more and reads a buffer
-                // nobody uses any more, so every slice takes the same path.
-                sync_slice(min(KT - 2 - kt, DSTAGES - 2));
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            const char* src = ks + 1 < KS ? s : lds[(kt + 1) % DSTAGES];
-            const int nks = ks + 1 < KS ? ks + 1 : 0;
-            if (even) read_frags(src, nks, fa1, fb1);  // KS is even: sets alternate 0, 1, 0, 1
-            else read_frags(src, nks, fa0, fb0);
-            if (REFILL && ks < NSPREAD) dma_rows<IPW>(obase, (uint32_t)obytes, goff, rkoff, rl, ks * DPS, (ks + 1) * DPS);
-            if (even) mfmas(fa0, fb0);
-            else mfmas(fa1, fb1);
-            // The DMAs write LDS, so the compiler keeps every fragment read ahead of
-            // them: reads go behind the first MFMAs, DMAs behind the following ones.
-#pragma unroll
-            for (int q = 0; q < NMF; ++q) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                if (q < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-                else if (REFILL && ks < NSPREAD && q - NRD < DPS)
-                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one DMA
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            __builtin_amdgcn_s_waitcnt(kLgkm0);
-        }
-    };
-    slice(0, std::false_type{});  // the prologue filled every buffer
-    int kt = 1;
-    for (; kt + DSTAGES - 1 < KT; ++kt) slice(kt, std::true_type{});
-    for (; kt < KT; ++kt) slice(kt, std::false_type{});
+    bf16x8 fa0[NA], fb0[BM], fa1[NA], fb1[BM];
 
+    // acc = the product over K slices kt0 .. kt0+nkt-1 of the tile whose rows goff holds.
+    auto compute = [&](int kt0, int nkt) {
 #pragma unroll
-    for (int i = 0; i < BN; ++i)
+        for (int i = 0; i < NA; ++i)
+#pragma unroll
+            for (int j = 0; j < BM; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+        // Prologue: every buffer requested; sub-step 0 of the first slice read.
+        for (int st = 0; st < DSTAGES && st < nkt; ++st)
+            dma_rows<IPW>(obase, (uint32_t)obytes, goff, (uint32_t)((kt0 + st) * DBK * 2), &lds[st][wrow0 * ROWB]);
+        sync_slice(min(nkt - 1, DSTAGES - 1));
+        read_frags(lds[0], 0, fa0, fb0);
+        // lgkmcnt has 4 bits: with two batches of reads outstanding the compiler could
+        // only wait for zero. Each batch is therefore drained (it had a whole MFMA
+        // phase to land, so this does not stall) before the next one is issued.
+        __builtin_amdgcn_s_waitcnt(kLgkm0);
+        auto slice = [&](int kt, auto refill_tag) {
+            constexpr bool REFILL = decltype(refill_tag)::value;
+            const char* s = lds[kt % DSTAGES];
+            const uint32_t rkoff = (uint32_t)((kt0 + kt - 1 + DSTAGES) * DBK * 2);
+            char* rl = &lds[(kt + DSTAGES - 1) % DSTAGES][wrow0 * ROWB];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bool even = (ks & 1) == 0;
+                if (ks + 1 == KS) {
+                    // On the last slice this synchronises once more and reads a buffer
+                    // nobody uses any more, so every slice takes the same path.
+                    sync_slice(min(nkt - 2 - kt, DSTAGES - 2));
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                const char* src = ks + 1 < KS ? s : lds[(kt + 1) % DSTAGES];
+                const int nks = ks + 1 < KS ? ks + 1 : 0;
+                if (even) read_frags(src, nks, fa1, fb1);  // KS is even: sets alternate 0, 1, 0, 1
+                else read_frags(src, nks, fa0, fb0);
+                if (REFILL && ks < NSPREAD)
+                    dma_rows<IPW>(obase, (uint32_t)obytes, goff, rkoff, rl, ks * DPS, (ks + 1) * DPS);
+                if (even) mfmas(fa0, fb0);
+                else mfmas(fa1, fb1);
+                // The DMAs write LDS, so the compiler keeps every fragment read ahead of
+                // them: reads go behind the first MFMAs, DMAs behind the following ones.
+#pragma unroll
+                for (int q = 0; q < NMF; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                    if (q < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+                    else if (REFILL && ks < NSPREAD && q - NRD < DPS)
+                        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one DMA
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_waitcnt(kLgkm0);
+            }
+        };
+        slice(0, std::false_type{});  // the prologue filled every buffer
+        int kt = 1;
+        for (; kt + DSTAGES - 1 < nkt; ++kt) slice(kt, std::true_type{});
+        for (; kt < nkt; ++kt) slice(kt, std::false_type{});
+    };
+
+    auto store_tile = [&](int n0, int m0) {
+#pragma unroll
+        for (int i = 0; i < BN; ++i)
+#pragma unroll
+            for (int j = 0; j < BM; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float gv[4], uv[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        gv[e] = acc[i][j][4 * q + e];
+                        uv[e] = SWIGLU ? acc[i + (SWIGLU ? BN : 0)][j][4 * q + e] : 0.f;
+                    }
+                    const int n_base = n0 + wn * WN + i * 32 + 8 * q + 4 * lh;
+                    const int m = m0 + wm * WM + j * 32 + l32;
+                    epilogue4<SWIGLU, BIAS, OutT>(p.o, n_base, m, gv, uv);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+    };
+
+    if (!SK) {
+        int tn, tm;
+        tile_of(blockIdx.x, p.tiles_n, p.tiles_m, tn, tm);
+        set_rows(tn * TN, tm * TM);
+        compute(0, KT);
+        store_tile(tn * TN, tm * TM);
+        return;
+    }
+
+    // Split tiles: piece q (XCD-major) is K range sp of split tile r. Its fp32
+    // partial tile goes to slot q of the work space as float4 groups [group][thread],
+    // so every 16-byte store covers contiguous memory; splitk_reduce_kernel, the next
+    // launch on the stream, sums the pieces.
+    constexpr int NT = NWAVES * 64;
+    constexpr int NG = NA * BM * 4;  // float4 groups per thread
+    const int R = p.tiles_n * p.tiles_m - p.F;
+    int tn, tm;
+    if ((int)blockIdx.x < p.F) {
+        tile_coords(xcd_major(blockIdx.x, p.F), p.tiles_n, p.tiles_m, tn, tm);
+        set_rows(tn * TN, tm * TM);
+        compute(0, KT);
+        store_tile(tn * TN, tm * TM);
+        return;
+    }
+    const int q = xcd_major((int)blockIdx.x - p.F, R * p.S);
+    const int sp = q / R, r = q - sp * R;
+    const int kt0 = (int)((int64_t)sp * KT / p.S), kt1 = (int)((int64_t)(sp + 1) * KT / p.S);
+    tile_coords(p.F + r, p.tiles_n, p.tiles_m, tn, tm);
+    set_rows(tn * TN, tm * TM);
+    compute(kt0, kt1 - kt0);
+    floatx4* dst = reinterpret_cast<floatx4*>(p.ws) + (int64_t)q * NG * NT + tid;
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
 #pragma unroll
         for (int j = 0; j < BM; ++j)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                float gv[4], uv[4];
+            for (int qq = 0; qq < 4; ++qq)
+                dst[((i * BM + j) * 4 + qq) * NT] = floatx4{acc[i][j][4 * qq], acc[i][j][4 * qq + 1],
+                                                          acc[i][j][4 * qq + 2], acc[i][j][4 * qq + 3]};
+}
+
+// The S pieces of each split tile, summed in K order, then the tile's epilogue.
+// Workgroup (r, i) takes block row i of split tile r with the thread layout of the
+// GEMM kernel, so thread tid reads exactly the float4 groups it would have held.
+template <int TN, int TM, int WAVES_N, int WAVES_M, bool SWIGLU, bool BIAS, typename OutT>
+__global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void splitk_reduce_kernel(GemmParams p) {
+    constexpr int NWAVES = WAVES_N * WAVES_M, NT = NWAVES * 64;
+    constexpr int WN = TN / WAVES_N, WM = TM / WAVES_M;
+    constexpr int BN = WN / 32, BM = WM / 32;
+    constexpr int NA = SWIGLU ? 2 * BN : BN;
+    constexpr int NG = NA * BM * 4;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wn = wave % WAVES_N, wm = wave / WAVES_N;
+    const int l32 = lane & 31, lh = lane >> 5;
+    const int R = p.tiles_n * p.tiles_m - p.F;
+    const int r = blockIdx.x / BN, i = blockIdx.x - r * BN;
+    int tn, tm;
+    tile_coords(p.F + r, p.tiles_n, p.tiles_m, tn, tm);
+    const floatx4* src = reinterpret_cast<const floatx4*>(p.ws) + (int64_t)r * NG * NT + tid;
+    const int64_t piece = (int64_t)R * NG * NT;  // float4s between pieces of one tile
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    gv[e] = acc[i][j][4 * q + e];
-                    uv[e] = SWIGLU ? acc[i + (SWIGLU ? BN : 0)][j][4 * q + e] : 0.f;
-                }
-                const int n_base = n0 + wn * WN + i * 32 + 8 * q + 4 * lh;
-                const int m = m0 + wm * WM + j * 32 + l32;
-                epilogue4<SWIGLU, BIAS, OutT>(p.o, n_base, m, gv, uv);
-                __builtin_amdgcn_sched_barrier(0);
+    for (int j = 0; j < BM; ++j) {
+        floatx4 g[4], u[4];
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+            g[qq] = src[((i * BM + j) * 4 + qq) * NT];
+            if (SWIGLU) u[qq] = src[(((i + (SWIGLU ? BN : 0)) * BM + j) * 4 + qq) * NT];
+        }
+        for (int sp = 1; sp < p.S; ++sp)
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                g[qq] += src[sp * piece + ((i * BM + j) * 4 + qq) * NT];
+                if (SWIGLU) u[qq] += src[sp * piece + (((i + (SWIGLU ? BN : 0)) * BM + j) * 4 + qq) * NT];
             }
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+            float gv[4], uv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                gv[e] = g[qq][e];
+                uv[e] = SWIGLU ? u[qq][e] : 0.f;
+            }
+            const int n_base = tn * TN + wn * WN + i * 32 + 8 * qq + 4 * lh;
+            const int m = tm * TM + wm * WM + j * 32 + l32;
+            epilogue4<SWIGLU, BIAS, OutT>(p.o, n_base, m, gv, uv);
+        }
+    }
 }
 
 template <int TN, int TM, int WAVES_N, int WAVES_M, bool SWIGLU, bool BIAS, typename OutT>
-tp_status_t run_dtl(const LinearDesc& d, hipStream_t stream) {
+tp_status_t run_dtl(const LinearDesc& d, int cus, hipStream_t stream) {
     GemmParams p;
     p.X = static_cast<const bf16*>(d.X);
     p.ldx = d.ldx;
@@ -491,20 +604,57 @@ tp_status_t run_dtl(const LinearDesc& d, hipStream_t stream) {
     p.K = (int)d.K;
     p.tiles_n = (int)ceil_div(d.N, TN);
     p.tiles_m = (int)ceil_div(d.M, TM);
+    p.F = 0;
+    p.S = 0;
+    p.ws = nullptr;
     const int64_t tiles = (int64_t)p.tiles_n * p.tiles_m;
-    hipLaunchKernelGGL((gemm_dtl_kernel<TN, TM, WAVES_N, WAVES_M, SWIGLU, BIAS, OutT>), dim3((unsigned)tiles),
-                       dim3(WAVES_N * WAVES_M * 64), 0, stream, p);
+    constexpr unsigned NT = WAVES_N * WAVES_M * 64;
+    // One tile per workgroup when whole waves of tiles fill the chip to 90 %. Else
+    // the whole waves stay one tile per workgroup and the R remaining tiles are cut
+    // into S K ranges, S (at most 4, at least 8 slices each) chosen so the pieces
+    // take the least time on `cus` CUs: ceil(R*S / cus) / S tile times. A split is
+    // only taken where it saves at least a third of a tile time: the partials cost
+    // a pass of their own.
+    const int64_t kt = d.K / DBK;
+    const int64_t F = tiles / cus * cus, R = tiles - F;
+    int S = 1;
+    if (R > 0 && tiles * 10 < ceil_div(tiles, (int64_t)cus) * cus * 9) {
+        double best = 2.0 / 3.0;
+        for (int s = 2; s <= 4 && kt / s >= 8; ++s) {
+            const double tm = (double)ceil_div(R * s, (int64_t)cus) / s;
+            if (tm < best - 1e-9) { best = tm; S = s; }
+        }
+    }
+    if (S == 1) {
+        hipLaunchKernelGGL((gemm_dtl_kernel<TN, TM, WAVES_N, WAVES_M, SWIGLU, BIAS, false, OutT>), dim3((unsigned)tiles),
+                           dim3(NT), 0, stream, p);
+        return hip_status();
+    }
+    constexpr int64_t TILEF = (int64_t)TN * (SWIGLU ? 2 : 1) * TM;  // floats of a partial tile
+    p.F = (int)F;
+    p.S = S;
+    Workspace ws;
+    tp_status_t st = get_workspace(stream, (size_t)(R * S * TILEF), 0, &ws);
+    if (st != TP_OK) return st;
+    p.ws = ws.partials;
+    hipLaunchKernelGGL((gemm_dtl_kernel<TN, TM, WAVES_N, WAVES_M, SWIGLU, BIAS, true, OutT>),
+                       dim3((unsigned)(F + R * S)), dim3(NT), 0, stream, p);
+    st = hip_status();
+    if (st != TP_OK) return st;
+    constexpr int BN = TN / WAVES_N / 32;
+    hipLaunchKernelGGL((splitk_reduce_kernel<TN, TM, WAVES_N, WAVES_M, SWIGLU, BIAS, OutT>), dim3((unsigned)(R * BN)),
+                       dim3(NT), 0, stream, p);
     return hip_status();
 }
 
 template <int TN, int TM, int WAVES_N, int WAVES_M, bool SWIGLU>
-tp_status_t run_dtl_bias(const LinearDesc& d, hipStream_t stream) {
+tp_status_t run_dtl_bias(const LinearDesc& d, int cus, hipStream_t stream) {
     const bool bias = d.b0 != nullptr;
     if (d.out_dtype == TP_DTYPE_BF16)
-        return bias ? run_dtl<TN, TM, WAVES_N, WAVES_M, SWIGLU, true, bf16>(d, stream)
-                    : run_dtl<TN, TM, WAVES_N, WAVES_M, SWIGLU, false, bf16>(d, stream);
-    return bias ? run_dtl<TN, TM, WAVES_N, WAVES_M, SWIGLU, true, float>(d, stream)
-                : run_dtl<TN, TM, WAVES_N, WAVES_M, SWIGLU, false, float>(d, stream);
+        return bias ? run_dtl<TN, TM, WAVES_N, WAVES_M, SWIGLU, true, bf16>(d, cus, stream)
+                    : run_dtl<TN, TM, WAVES_N, WAVES_M, SWIGLU, false, bf16>(d, cus, stream);
+    return bias ? run_dtl<TN, TM, WAVES_N, WAVES_M, SWIGLU, true, float>(d, cus, stream)
+                : run_dtl<TN, TM, WAVES_N, WAVES_M, SWIGLU, false, float>(d, cus, stream);
 }
 
 template <int TN, int TM, int WAVES_N, int WAVES_M, bool SWIGLU, bool BIAS, bool KTAIL, typename OutT>
@@ -562,21 +712,24 @@ tp_status_t launch_gemm(const LinearDesc& d, hipStream_t stream) {
             hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
             cus = n;
     }
-    // 256 x 256 tiles (4 waves of 128 x 128, one workgroup per CU) when they fill the
-    // chip, else 128 x 128 tiles (4 waves of 64 x 64, two workgroups per CU).
-    // Large tiles use the LDS-DMA kernel when K is a whole number of slices.
+    // Large tiles (256 x 256, or 128 x 256 with the SwiGLU pair: 4 waves of 128 x 128
+    // outputs, one workgroup per CU) when they fill the chip; with K a whole number
+    // of slices they run on the LDS-DMA kernel, which also takes fewer tiles than CUs
+    // once each CU gets at least 16 slices of stream-K work. Otherwise 128 x 128
+    // tiles (4 waves of 64 x 64, two workgroups per CU).
     const bool dma = d.K % DBK == 0;
+    const int64_t kt = d.K / DBK;
     if (d.swiglu) {
         const int64_t big = ceil_div(d.N, 128) * ceil_div(d.M, 256);
-        if (big >= cus)
-            return dma ? run_dtl_bias<128, 256, 2, TP_DMA_WAVES_M, true>(d, stream)
-                       : run_bias<128, 256, 2, 2, true>(d, stream);
+        if (dma && (big >= cus || big * kt >= 16 * (int64_t)cus))
+            return run_dtl_bias<128, 256, 2, TP_DMA_WAVES_M, true>(d, cus, stream);
+        if (big >= cus) return run_bias<128, 256, 2, 2, true>(d, stream);
         return run_bias<64, 128, 2, 2, true>(d, stream);
     }
     const int64_t big = ceil_div(d.N, 256) * ceil_div(d.M, 256);
-    if (big >= cus)
-        return dma ? run_dtl_bias<256, 256, 2, TP_DMA_WAVES_M, false>(d, stream)
-                   : run_bias<256, 256, 2, 2, false>(d, stream);
+    if (dma && (big >= cus || big * kt >= 16 * (int64_t)cus))
+        return run_dtl_bias<256, 256, 2, TP_DMA_WAVES_M, false>(d, cus, stream);
+    if (big >= cus) return run_bias<256, 256, 2, 2, false>(d, stream);
     return run_bias<128, 128, 2, 2, false>(d, stream);
 }
 

@@ -295,7 +295,7 @@ def test_shard_weight_exact():
 
 # ---- determinism, M = 0, error path on the device ------------------------------------------
 
-@pytest.mark.parametrize("M,K,N", [(1, 8192, 1280), (64, 4096, 688), (300, 2048, 520)])
+@pytest.mark.parametrize("M,K,N", [(1, 8192, 1280), (64, 4096, 688), (300, 2048, 520), (1000, 16384, 1320)])
 def test_bitwise_deterministic(M, K, N):
     log_case("deterministic", M, K, N)
     x, w, b = I.activations(M, K, 1), I.weight(N, K, 2), I.bias(N, 3)
@@ -332,6 +332,7 @@ def test_errors_raise_before_launch():
 
 DMA_SHAPES = [  # (M, K, N): tails in M and N, K a multiple of 64
     (2100, 1024, 8168), (4096 + 33, 576, 8192 - 40), (8192, 128, 8192 + 8),
+    (4096 - 40, 1024, 8192 - 24),  # 512 tiles: one tile per workgroup, ragged edges
 ]
 
 
@@ -359,6 +360,50 @@ def test_dma_kernel_swiglu_tails(M, K, I_):
     x = I.activations(M, K, 311)
     wg, wu = I.weight(I_, K, 312), I.weight(I_, K, 313)
     bg, bu = I.bias(I_, 314), I.bias(I_, 315)
+    buf, H = canary_buffer((M, I_), torch.bfloat16)
+    tp.tp_mlp_shard(dev(x), dev(wg), dev(wu), dev(bg), dev(bu), None, H, None, M, K, I_, 1)
+    torch.cuda.synchronize()
+    rows = _sample_rows(M)
+    xs = host64(x)[rows]
+    ref = O.swiglu(O.linear(xs, host64(wg), host64(bg)), O.linear(xs, host64(wu), host64(bu)))
+    assert err(H.cpu()[rows], ref) <= BF16_TOL
+    assert canaries_intact(buf, (M, I_))
+
+
+# ---- stream-K: fewer large tiles than CUs, so K is shared between workgroups ---------------
+# (the LDS-DMA kernel takes these once every CU gets at least 16 slices of 64).
+
+@pytest.mark.parametrize("M,K,N", [(1000, 16384, 1320), (2048, 8192, 1280), (4096, 8192, 1280)])
+def test_stream_k_linear(M, K, N):
+    log_case("stream-K linear", M, K, N)
+    x, w, b = I.activations(M, K, 321), I.weight(N, K, 322), I.bias(N, 323)
+    buf, Y = canary_buffer((M, N), torch.bfloat16)
+    tp.tp_linear_col(dev(x), dev(w), dev(b), Y, M, K, N, 1)
+    torch.cuda.synchronize()
+    rows = _sample_rows(M)
+    ref = O.linear(host64(x)[rows], host64(w), host64(b))
+    assert err(Y.cpu()[rows], ref) <= BF16_TOL
+    assert canaries_intact(buf, (M, N))
+
+
+def test_stream_k_partial_fp32():
+    M, K, N = 1000, 16384, 1320
+    log_case("stream-K fp32 partial", M, K, N)
+    x, w = I.activations(M, K, 331), I.weight(N, K, 332)
+    P = torch.empty(M, N, dtype=torch.float32, device="cuda")
+    tp.tp_linear_row_partial(dev(x), K, dev(w), P, M, K * 2, N, 2)
+    torch.cuda.synchronize()
+    rows = _sample_rows(M)
+    ref = O.linear(host64(x)[rows], host64(w), None)
+    assert err(P.cpu()[rows], ref) <= BF16_TOL
+
+
+@pytest.mark.parametrize("M,K,I_", [(1000, 8192, 1000), (4096, 8192, 3584)])
+def test_stream_k_swiglu(M, K, I_):
+    log_case("stream-K swiglu", M, K, I_)
+    x = I.activations(M, K, 341)
+    wg, wu = I.weight(I_, K, 342), I.weight(I_, K, 343)
+    bg, bu = I.bias(I_, 344), I.bias(I_, 345)
     buf, H = canary_buffer((M, I_), torch.bfloat16)
     tp.tp_mlp_shard(dev(x), dev(wg), dev(wu), dev(bg), dev(bu), None, H, None, M, K, I_, 1)
     torch.cuda.synchronize()
