@@ -307,6 +307,7 @@ __device__ __forceinline__ void dma_rows(const void* base, uint32_t bytes, const
 template <int TN, int TM, int WAVES_N, int WAVES_M, bool SWIGLU, bool BIAS, bool SK, typename OutT>
 __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void gemm_dtl_kernel(GemmParams p) {
     constexpr int NWAVES = WAVES_N * WAVES_M;
+    constexpr int NT = NWAVES * 64;
     constexpr int WN = TN / WAVES_N, WM = TM / WAVES_M;
     constexpr int BN = WN / 32, BM = WM / 32;
     constexpr int NA = SWIGLU ? 2 * BN : BN;
@@ -326,7 +327,13 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void gemm_dtl_kernel(GemmPar
     static_assert(TN % (IPW * RPI) == 0 && WROWS % (IPW * RPI) == 0, "a wave's rows come from one operand");
     static_assert(32 % (RPW * CPR) == 0, "swizzle period divides a 32-row block");
 
-    __shared__ __attribute__((aligned(1024))) char lds[DSTAGES][STAGEB];
+    // The LDS ring, which also stages a plain bf16 output tile (rows padded by 16
+    // bytes) so the tile leaves in whole 16-byte runs of each output row.
+    constexpr int OPITCH = TN * 2 + 16;
+    constexpr int OBYTES = SWIGLU ? 0 : TM * OPITCH;
+    constexpr int LDSB = DSTAGES * STAGEB > OBYTES ? DSTAGES * STAGEB : OBYTES;
+    __shared__ __attribute__((aligned(1024))) char lds_raw[LDSB];
+    auto lds = reinterpret_cast<char (*)[STAGEB]>(lds_raw);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -477,6 +484,54 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void gemm_dtl_kernel(GemmPar
     };
 
     auto store_tile = [&](int n0, int m0) {
+        // Measured: staging pays for plain tiles (256 B of each output row per wave
+        // and block row otherwise goes out 8 bytes at a time) but not for SwiGLU
+        // ones, whose epilogue arithmetic then sits between two barriers.
+        if (!SWIGLU && std::is_same<OutT, bf16>::value && p.o.vec16) {
+            // Every wave is past its last LDS read of the ring.
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < BN; ++i)
+#pragma unroll
+                for (int j = 0; j < BM; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        float gv[4], uv[4], y[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            gv[e] = acc[i][j][4 * q + e];
+                            uv[e] = SWIGLU ? acc[i + (SWIGLU ? BN : 0)][j][4 * q + e] : 0.f;
+                        }
+                        const int nl = wn * WN + i * 32 + 8 * q + 4 * lh;
+                        const int ml = wm * WM + j * 32 + l32;
+                        epilogue_vals4<SWIGLU, BIAS>(p.o, n0 + nl, gv, uv, y);
+                        const bf16x4 v = {(bf16)y[0], (bf16)y[1], (bf16)y[2], (bf16)y[3]};
+                        *reinterpret_cast<bf16x4*>(lds_raw + ml * OPITCH + nl * 2) = v;
+                    }
+            __syncthreads();
+            // Each pass writes NT/CPRW whole rows of the tile, 16 bytes per thread.
+            constexpr int CPRW = TN * 2 / 16;  // 16-byte chunks per output row
+            constexpr int RPP = NT / CPRW;
+            static_assert(NT % CPRW == 0 && TM % RPP == 0, "whole rows per pass");
+            const int c = tid % CPRW;
+            const int n = n0 + c * 8;
+#pragma unroll 4
+            for (int r0 = 0; r0 < TM; r0 += RPP) {
+                const int row = r0 + tid / CPRW;
+                const int m = m0 + row;
+                if (m >= p.o.M) continue;
+                const bf16x8 v = *reinterpret_cast<const bf16x8*>(lds_raw + row * OPITCH + c * 16);
+                bf16* dst = reinterpret_cast<bf16*>(p.o.Y) + (int64_t)m * p.o.ldy + n;
+                if (n + 8 <= p.o.N) {
+                    *reinterpret_cast<bf16x8*>(dst) = v;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (n + e < p.o.N) dst[e] = v[e];
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < BN; ++i)
 #pragma unroll
@@ -509,7 +564,6 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void gemm_dtl_kernel(GemmPar
     // partial tile goes to slot q of the work space as float4 groups [group][thread],
     // so every 16-byte store covers contiguous memory; splitk_reduce_kernel, the next
     // launch on the stream, sums the pieces.
-    constexpr int NT = NWAVES * 64;
     constexpr int NG = NA * BM * 4;  // float4 groups per thread
     const int R = p.tiles_n * p.tiles_m - p.F;
     int tn, tm;
@@ -599,6 +653,7 @@ tp_status_t run_dtl(const LinearDesc& d, int cus, hipStream_t stream) {
     p.o.b0 = static_cast<const bf16*>(d.b0);
     p.o.b1 = static_cast<const bf16*>(d.b1);
     p.o.vec_store = vec_store_ok<OutT>(d.Y, d.ldy);
+    p.o.vec16 = vec16_ok<OutT>(d.Y, d.ldy);
     p.M = (int)d.M;
     p.N = (int)d.N;
     p.K = (int)d.K;
@@ -671,6 +726,7 @@ tp_status_t run(const LinearDesc& d, hipStream_t stream) {
     p.o.b0 = static_cast<const bf16*>(d.b0);
     p.o.b1 = static_cast<const bf16*>(d.b1);
     p.o.vec_store = vec_store_ok<OutT>(d.Y, d.ldy);
+    p.o.vec16 = vec16_ok<OutT>(d.Y, d.ldy);
     p.M = (int)d.M;
     p.N = (int)d.N;
     p.K = (int)d.K;

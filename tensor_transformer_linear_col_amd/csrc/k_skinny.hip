@@ -297,6 +297,7 @@ tp_status_t run(const LinearDesc& d, hipStream_t stream) {
     p.o.b0 = static_cast<const bf16*>(d.b0);
     p.o.b1 = static_cast<const bf16*>(d.b1);
     p.o.vec_store = vec_store_ok<OutT>(d.Y, d.ldy);
+    p.o.vec16 = vec16_ok<OutT>(d.Y, d.ldy);
     p.M = (int)d.M;
     p.N = (int)d.N;
     p.K = (int)d.K;

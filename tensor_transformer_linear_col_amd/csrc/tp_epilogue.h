@@ -12,6 +12,7 @@ struct OutDesc {
     const bf16* b0;  // bias of the (gate) product, or nullptr
     const bf16* b1;  // bias of the up product (SwiGLU), or nullptr
     int vec_store;   // 1 when 4 consecutive outputs may be written as one vector
+    int vec16;       // 1 when 16-byte aligned runs of a row may be written as one vector
 };
 
 template <typename OutT>
@@ -41,13 +42,12 @@ __device__ __forceinline__ void store_out4<float>(float* row, int n_base, int N,
     }
 }
 
-// Four consecutive outputs n_base..n_base+3 of token row m, from fp32 sums g (and u).
+// Four consecutive outputs n_base..n_base+3 from fp32 sums g (and u):
 //   plain:  y = g + b0[n]
 //   SwiGLU: y = silu(g + b0[n]) * (u + b1[n]),  silu(z) = z / (1 + exp(-z))
-template <bool SWIGLU, bool BIAS, typename OutT>
-__device__ __forceinline__ void epilogue4(const OutDesc& o, int n_base, int m, const float g[4], const float u[4]) {
-    if (m >= o.M) return;
-    float y[4];
+template <bool SWIGLU, bool BIAS>
+__device__ __forceinline__ void epilogue_vals4(const OutDesc& o, int n_base, const float g[4], const float u[4],
+                                               float y[4]) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int n = n_base + e;
@@ -59,6 +59,14 @@ __device__ __forceinline__ void epilogue4(const OutDesc& o, int n_base, int m, c
         }
         y[e] = SWIGLU ? a / (1.f + expf(-a)) * c : a;
     }
+}
+
+// The same four outputs of token row m, rounded once to OutT and stored.
+template <bool SWIGLU, bool BIAS, typename OutT>
+__device__ __forceinline__ void epilogue4(const OutDesc& o, int n_base, int m, const float g[4], const float u[4]) {
+    if (m >= o.M) return;
+    float y[4];
+    epilogue_vals4<SWIGLU, BIAS>(o, n_base, g, u, y);
     OutT* row = reinterpret_cast<OutT*>(o.Y) + (int64_t)m * o.ldy;
     store_out4<OutT>(row, n_base, o.N, y, o.vec_store != 0);
 }
@@ -66,6 +74,11 @@ __device__ __forceinline__ void epilogue4(const OutDesc& o, int n_base, int m, c
 template <typename OutT>
 inline int vec_store_ok(const void* Y, int64_t ldy) {
     return ((uintptr_t)Y % (4 * sizeof(OutT)) == 0 && ldy % 4 == 0) ? 1 : 0;
+}
+
+template <typename OutT>
+inline int vec16_ok(const void* Y, int64_t ldy) {
+    return ((uintptr_t)Y % 16 == 0 && (ldy * (int64_t)sizeof(OutT)) % 16 == 0) ? 1 : 0;
 }
 
 }  // namespace tp

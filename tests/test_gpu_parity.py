@@ -333,6 +333,7 @@ def test_errors_raise_before_launch():
 DMA_SHAPES = [  # (M, K, N): tails in M and N, K a multiple of 64
     (2100, 1024, 8168), (4096 + 33, 576, 8192 - 40), (8192, 128, 8192 + 8),
     (4096 - 40, 1024, 8192 - 24),  # 512 tiles: one tile per workgroup, ragged edges
+    (4096, 256, 8190),  # output rows not a whole number of 16-byte runs: per-element stores
 ]
 
 
