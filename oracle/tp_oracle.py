@@ -38,6 +38,8 @@ Parity status per function (what pins it, beside itself):
       output, brute-force fsum, closed-form special cases, page invariants).
   silu / swiglu:  pinned by closed forms of the definition; the choice of
       SwiGLU over GELU is a reading.
+  gelu / ffn_gelu:  gelu pinned by closed forms (odd-part identity, tabulated
+      normal CDF values); the FFN by the sharded-equals-unsharded invariant.
   qkv head layout / attention stand-in (A := Q):  parity unpinned by the
       pages (self-consistency invariants only).
 """
@@ -201,6 +203,23 @@ def swiglu(g, u) -> np.ndarray:
     return silu(g) * f64(u)
 
 
+def gelu(z) -> np.ndarray:
+    """The exact (erf) GELU that the listing's FFN applies between its column and row
+    layers ([P3] "Implementing Tensor Parallelism with Hugging Face Accelerate",
+    torch.nn.functional.gelu with its default form): gelu(z) = z * Phi(z), with
+    Phi the standard normal CDF, Phi(z) = (1 + erf(z / sqrt(2))) / 2."""
+    z = f64(z)
+    return 0.5 * z * (1.0 + _erf(z / math.sqrt(2.0)))
+
+
+def _erf(z) -> np.ndarray:
+    try:
+        from scipy.special import erf
+        return erf(z)
+    except ImportError:  # pragma: no cover - scipy is present in this image
+        return np.vectorize(math.erf)(z)
+
+
 # ---------------------------------------------------------------------------
 # Paired column -> row MLP ([P3] "How Tensor Parallelism Works Under the Hood":
 # first layer column-parallel, second row-parallel; [P5] researcher section:
@@ -227,6 +246,30 @@ def mlp_shards(x, wg, wu, wd, p, bg=None, bu=None):
         wu_r, bu_r = col_shard(wu, bu, p, r)
         wd_r = row_shard(wd, p, r)
         out.append(mlp_shard(x, wg_r, wu_r, wd_r, bg_r, bu_r))
+    return out
+
+
+# The listing's own FFN ([P3] "Implementing Tensor Parallelism with Hugging Face
+# Accelerate": a ColumnParallelLinear 4096 -> 11008, GELU, a RowParallelLinear
+# 11008 -> 4096 whose bias is added once after the reduction)
+
+def ffn_gelu(x, w1, w2, b1=None, b2=None):
+    """Unsharded: Y = gelu(X W1^T + b1) W2^T + b2."""
+    return linear(gelu(linear(x, w1, b1)), w2, b2)
+
+
+def ffn_gelu_shard(x, w1_r, w2_r, b1_r=None):
+    """Shard r: H_r = gelu(X W1_r^T + b1_r) (column), P_r = H_r W2_r^T (row partial, no bias)."""
+    h_r = gelu(col_linear(x, w1_r, b1_r))
+    return h_r, row_partial(h_r, w2_r)
+
+
+def ffn_gelu_shards(x, w1, w2, p, b1=None):
+    """All p shards, from slices of the unsharded weights."""
+    out = []
+    for r in range(p):
+        w1_r, b1_r = col_shard(w1, b1, p, r)
+        out.append(ffn_gelu_shard(x, w1_r, row_shard(w2, p, r), b1_r))
     return out
 
 

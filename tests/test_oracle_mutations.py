@@ -38,6 +38,16 @@ def _silu_sigmoid_only(z):
         return 1.0 / (1.0 + np.exp(-z))
 
 
+def _gelu_tanh_approximation(z):
+    z = T.f64(z)
+    return 0.5 * z * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (z + 0.044715 * z ** 3)))
+
+
+def _gelu_erf_unscaled(z):
+    z = T.f64(z)
+    return 0.5 * z * (1.0 + T._erf(z))
+
+
 def _combine_sum_bias_each(partials, b=None):
     acc = np.zeros_like(T.f64(partials[0]))
     for p_r in partials:
@@ -83,6 +93,8 @@ MUTATIONS = [
                                     P.test_identity_weight_returns_input_plus_bias]),
     ("silu", _silu_wrong_sign, [P.test_silu_closed_forms, P.test_mlp_tiny_by_bruteforce]),
     ("silu", _silu_sigmoid_only, [P.test_silu_closed_forms, P.test_swiglu_special_cases]),
+    ("gelu", _gelu_tanh_approximation, [P.test_gelu_closed_forms]),
+    ("gelu", _gelu_erf_unscaled, [P.test_gelu_closed_forms, P.test_gelu_ffn_tiny_by_bruteforce]),
     ("combine_sum", _combine_sum_bias_each, [P.test_toy_row_split_sum_plus_bias_equals_unsharded]),
     ("combine_sum", _combine_sum_drop_last, [P.test_toy_row_split_sum_plus_bias_equals_unsharded]),
     ("col_shard", _col_shard_off_by_one, [P.test_toy_column_split_concat_matches_printed_values_and_is_exact]),

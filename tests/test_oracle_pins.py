@@ -147,6 +147,21 @@ def test_swiglu_special_cases():
     np.testing.assert_allclose(O.swiglu(np.full((1, 3), ln3), u), 0.75 * ln3 * u, rtol=1e-15)
 
 
+def test_gelu_closed_forms():
+    # gelu(z) = z * Phi(z); tabulated standard normal CDF: Phi(1) = 0.8413447460685429,
+    # Phi(2) = 0.9772498680518208, Phi(-1) = 1 - Phi(1).
+    z = np.array([0.0, 1.0, -1.0, 2.0, 10.0, -10.0])
+    g = O.gelu(z)
+    assert g[0] == 0.0
+    assert abs(g[1] - 0.8413447460685429) < 1e-15
+    assert abs(g[2] + (1.0 - 0.8413447460685429)) < 1e-15
+    assert abs(g[3] - 2.0 * 0.9772498680518208) < 1e-15
+    assert abs(g[4] - 10.0) < 1e-12             # gelu(z) -> z for z >> 0
+    assert abs(g[5]) < 1e-20                    # gelu(z) -> 0 for z << 0
+    zz = np.linspace(-6, 6, 97)
+    np.testing.assert_allclose(O.gelu(zz) - O.gelu(-zz), zz, atol=1e-14)  # z*Phi(z) + z*Phi(-z) = z
+
+
 # --- invariants the pages state ---------------------------------------------------------
 
 def test_bias_added_to_every_partial_is_off_by_p_minus_1_times_b():
@@ -216,6 +231,32 @@ def test_mlp_tiny_by_bruteforce():
     hh = np.array([[gv / (1.0 + math.exp(-gv)) * uv for gv, uv in zip(gr, ur)] for gr, ur in zip(g, u)])
     y_bf = O.linear_fsum(hh, wt["Wd"], wt["bd"])
     y = O.mlp(x, wt["Wg"], wt["Wu"], wt["Wd"], wt["bg"], wt["bu"], wt["bd"])
+    np.testing.assert_allclose(y, y_bf, rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("p", [2, 4])
+def test_gelu_ffn_pairing_sum_of_partials_equals_unsharded(p):
+    """The listing's FFN: column layer, GELU, row layer; one sum and the bias at the end."""
+    h, i, m = 32, 64, 4
+    shape = I.LayerShape("t", hidden=h, intermediate=i, tp=p, seed=9)
+    wt = {k: I.as_numpy_f64(v) for k, v in I.gelu_ffn_weights(shape).items()}
+    x = I.as_numpy_f64(I.activations(m, h, seed=91))
+    ref = O.ffn_gelu(x, wt["W1"], wt["W2"], wt["b1"], wt["b2"])
+    shards = O.ffn_gelu_shards(x, wt["W1"], wt["W2"], p, wt["b1"])
+    y = O.combine_sum([pr for _, pr in shards], wt["b2"])
+    assert O.rel_err(y, ref) <= 1e-13
+    np.testing.assert_array_equal(O.concat([h_r for h_r, _ in shards]), O.gelu(O.linear(x, wt["W1"], wt["b1"])))
+
+
+def test_gelu_ffn_tiny_by_bruteforce():
+    h, i, m = 6, 8, 2
+    shape = I.LayerShape("t", hidden=h, intermediate=i, tp=2, seed=10)
+    wt = {k: I.as_numpy_f64(v) for k, v in I.gelu_ffn_weights(shape).items()}
+    x = I.as_numpy_f64(I.activations(m, h, seed=101))
+    a = O.linear_fsum(x, wt["W1"], wt["b1"])
+    hh = np.array([[0.5 * v * (1.0 + math.erf(v / math.sqrt(2.0))) for v in row] for row in a])
+    y_bf = O.linear_fsum(hh, wt["W2"], wt["b2"])
+    y = O.ffn_gelu(x, wt["W1"], wt["W2"], wt["b1"], wt["b2"])
     np.testing.assert_allclose(y, y_bf, rtol=1e-12, atol=1e-14)
 
 

@@ -55,8 +55,13 @@ LLAMA70B_LAYER_TP8 = LayerShape("llama70b-layer-prefill-tp8", hidden=8192, inter
                                 n_heads=64, n_kv_heads=8, head_dim=128, tp=8, tokens=(4096,),
                                 seed=5)
 
+# The pages' own FFN: 4096 -> 11008 -> 4096 with GELU between the column and the
+# row layer, batch 4, here at TP = 2.
+PAGES_FFN_GELU_TP2 = LayerShape("pages-ffn-gelu-tp2", hidden=4096, intermediate=11008, tp=2,
+                                tokens=(4,), seed=6)
+
 CONFIGS = {s.name: s for s in (TOY, LLAMA7B_FFN_TP2, LLAMA70B_FFN_TP4, LLAMA70B_ATTN_TP8,
-                                LLAMA70B_LAYER_TP8)}
+                                LLAMA70B_LAYER_TP8, PAGES_FFN_GELU_TP2)}
 
 
 def _gen(seed: int) -> torch.Generator:
@@ -116,6 +121,7 @@ def activation_seed(cfg_seed: int, m: int, slot: int = 0) -> int:
 # Tensor slots within a configuration (fixed so every caller draws the same values).
 SLOT_WQKV, SLOT_BQKV, SLOT_WO, SLOT_BO = 1, 2, 3, 4
 SLOT_WG, SLOT_BG, SLOT_WU, SLOT_BU, SLOT_WD, SLOT_BD = 5, 6, 7, 8, 9, 10
+SLOT_W1, SLOT_B1, SLOT_W2, SLOT_B2 = 11, 12, 13, 14
 
 
 def ffn_weights(shape: LayerShape, dtype=torch.bfloat16, with_bias: bool = True,
@@ -133,6 +139,22 @@ def ffn_weights(shape: LayerShape, dtype=torch.bfloat16, with_bias: bool = True,
         out["bg"] = bias(i, tensor_seed(s, SLOT_BG), dtype)
         out["bu"] = bias(i, tensor_seed(s, SLOT_BU), dtype)
         out["bd"] = bias(h, tensor_seed(s, SLOT_BD), dtype)
+    return out
+
+
+def gelu_ffn_weights(shape: LayerShape, dtype=torch.bfloat16, with_bias: bool = True,
+                     hidden: int | None = None, intermediate: int | None = None):
+    """Unsharded GELU FFN weights: W1 [I, H] (column layer), W2 [H, I] (row layer); b1 [I], b2 [H]."""
+    h = hidden or shape.hidden
+    i = intermediate or shape.intermediate
+    s = shape.seed
+    out = {
+        "W1": weight(i, h, tensor_seed(s, SLOT_W1), dtype),
+        "W2": weight(h, i, tensor_seed(s, SLOT_W2), dtype),
+    }
+    if with_bias:
+        out["b1"] = bias(i, tensor_seed(s, SLOT_B1), dtype)
+        out["b2"] = bias(h, tensor_seed(s, SLOT_B2), dtype)
     return out
 
 
