@@ -222,6 +222,51 @@ def decode_bench(iters=30):
             log(f"decode {shape.name} M={M}: gate/up {gu*1e3:.1f} us, down {dn*1e3:.1f} us")
         del sets, base
         torch.cuda.empty_cache()
+
+    # The pages' own FFN (GELU between the column and the row layer), batch 4, TP = 2.
+    shape = I.PAGES_FFN_GELU_TP2
+    h, inter, p = shape.hidden, shape.intermediate, shape.tp
+    i = inter // p
+    wt = I.gelu_ffn_weights(shape, with_bias=True)
+    shard_bytes = 2 * i * h * 2
+    copies = max(1, -(-(1 << 30) // shard_bytes) + 1)
+    base = [(wt["W1"][r * i:(r + 1) * i].contiguous().cuda(), wt["b1"][r * i:(r + 1) * i].contiguous().cuda(),
+             wt["W2"][:, r * i:(r + 1) * i].contiguous().cuda()) for r in range(p)]
+    sets = [base[c % p] if c < p else tuple(t.clone() for t in base[c % p]) for c in range(copies)]
+    del wt
+    for M in shape.tokens:
+        x = I.activations(M, h, I.activation_seed(shape.seed, M)).cuda()
+        H = torch.empty(M, i, dtype=BF, device="cuda")
+        P = torch.empty(M, h, dtype=BF, device="cuda")
+        for c in range(len(sets)):  # warm
+            W1, b1, W2 = sets[c]
+            tp.tp_ffn_gelu_shard(x, W1, b1, None, H, None, M, h, inter, p)
+        torch.cuda.synchronize()
+        hold_gpu(5e-3)
+        ev_c, ev_r = [], []
+        for it in range(iters):
+            W1, b1, W2 = sets[it % len(sets)]
+            a, b, c2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            a.record()
+            tp.tp_ffn_gelu_shard(x, W1, b1, None, H, None, M, h, inter, p)
+            b.record()
+            tp.tp_linear_row_partial(H, i, W2, P, M, inter, h, p)
+            c2.record()
+            ev_c.append((a, b))
+            ev_r.append((b, c2))
+        torch.cuda.synchronize()
+        cu = sorted(a.elapsed_time(b) for a, b in ev_c)[len(ev_c) // 2]
+        rw = sorted(a.elapsed_time(b) for a, b in ev_r)[len(ev_r) // 2]
+        cu_bytes = i * h * 2 + i * 2 + M * h * 2 + M * i * 2
+        rw_bytes = h * i * 2 + M * i * 2 + M * h * 2
+        for op, ms, by, fl in (("col_gelu", cu, cu_bytes, 2.0 * M * i * h), ("row_partial", rw, rw_bytes, 2.0 * M * h * i)):
+            gbs = by / (ms * 1e-3) / 1e9
+            results.append({"workload": shape.name, "M": M, "op": op, "us": round(ms * 1e3, 2),
+                            "GB_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 3),
+                            "TFLOP_s": round(fl / (ms * 1e-3) / 1e12, 2)})
+        log(f"decode {shape.name} M={M}: column+gelu {cu*1e3:.1f} us, row {rw*1e3:.1f} us")
+    del sets, base
+    torch.cuda.empty_cache()
     return results
 
 

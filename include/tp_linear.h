@@ -109,6 +109,20 @@ tp_status_t tp_mlp_shard(const void* X, const void* Wg_r, const void* Wu_r,
                          int32_t tp_size, tp_dtype_t dtype, tp_dtype_t partial_dtype,
                          void* stream);
 
+/* The pages' own FFN, shard r ([P3] "Implementing Tensor Parallelism with Hugging Face
+ * Accelerate": a ColumnParallelLinear hidden -> intermediate, GELU, a RowParallelLinear
+ * intermediate -> hidden; its example is 4096 -> 11008 -> 4096 at batch 4):
+ *   H_r[M, I/p]    = gelu(X * W1_r^T + b1_r),  gelu(z) = z * (1 + erf(z / sqrt(2))) / 2
+ *   P_r[M, hidden] = H_r * W2_r^T   (partial, no bias; skipped when P_r is NULL)
+ *   X : [M, hidden]; W1_r : [I/p, hidden]; b1_r : [I/p] or NULL; W2_r : [hidden, I/p]
+ *   (may be NULL when P_r is NULL); H_r is always written. The listing slices the row
+ *   layer's input by rank a second time; here the row layer takes the shard's own H_r.
+ * TP_ERR_INDIVISIBLE if intermediate % tp_size != 0. Errors as for tp_mlp_shard. */
+tp_status_t tp_ffn_gelu_shard(const void* X, const void* W1_r, const void* b1_r, const void* W2_r,
+                              void* H_r, void* P_r, int64_t M, int64_t hidden, int64_t intermediate,
+                              int32_t tp_size, tp_dtype_t dtype, tp_dtype_t partial_dtype,
+                              void* stream);
+
 /* Head-split attention projections, shard r ([P4] "How a layer is split": heads go to
  * different GPUs and the TP size divides the heads; [P5] one sum per attention block).
  *   QKV_r[M, (Hq/p + 2*G/p)*d] = X * Wqkv_r^T + bqkv_r   (skipped when QKV_r is NULL)

@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "TP_DTYPE_F32", "TP_DTYPE_BF16", "TPError", "lib", "lib_path", "tp_linear_col",
-    "tp_linear_row_partial", "tp_mlp_shard", "tp_attn_proj_shard", "tp_combine_concat",
+    "tp_linear_row_partial", "tp_mlp_shard", "tp_ffn_gelu_shard", "tp_attn_proj_shard", "tp_combine_concat",
     "tp_combine_sum", "tp_shard_weight", "tp_shard_qkv", "tp_release_workspaces",
     "tp_status_string", "EXPORTS",
 ]
@@ -33,6 +33,7 @@ _SIGS = {
     "tp_linear_col": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp],
     "tp_linear_row_partial": [_vp, _i64, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp],
     "tp_mlp_shard": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp],
+    "tp_ffn_gelu_shard": [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp],
     "tp_attn_proj_shard": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _i32, _i32, _i32,
                            _i32, _vp],
     "tp_combine_concat": [ctypes.POINTER(_vp), _i32, ctypes.POINTER(_i64), _i32, _vp, _i64, _i32, _vp],
@@ -156,6 +157,22 @@ def tp_mlp_shard(X, Wg_r, Wu_r, bg_r, bu_r, Wd_r, H_r, P_r, M: int, hidden: int,
           _dev(bg_r, "bg_r", i if need else None),
           _dev(bu_r, "bu_r", i if need else None),
           _dev(Wd_r, "Wd_r", hidden * i if need and P_r is not None else None),
+          _dev(H_r, "H_r", M * i if need else None),
+          _dev(P_r, "P_r", M * hidden if need else None),
+          M, hidden, intermediate, tp_size, _dt(X), pdt, _stream())
+
+
+def tp_ffn_gelu_shard(X, W1_r, b1_r, W2_r, H_r, P_r, M: int, hidden: int, intermediate: int,
+                      tp_size: int, partial_dtype=None) -> None:
+    """H_r = gelu(X W1_r^T + b1_r) (erf form); P_r = H_r W2_r^T (partial)."""
+    i = _div(intermediate, tp_size)
+    need = i is not None and M > 0
+    pdt = (_dt(P_r) if P_r is not None else _dt(X)) if partial_dtype is None else partial_dtype
+    _call("tp_ffn_gelu_shard",
+          _dev(X, "X", M * hidden if need else None),
+          _dev(W1_r, "W1_r", i * hidden if need else None),
+          _dev(b1_r, "b1_r", i if need else None),
+          _dev(W2_r, "W2_r", hidden * i if need and P_r is not None else None),
           _dev(H_r, "H_r", M * i if need else None),
           _dev(P_r, "P_r", M * hidden if need else None),
           M, hidden, intermediate, tp_size, _dt(X), pdt, _stream())

@@ -20,6 +20,7 @@ struct F32Params {
     float* Y;
     int64_t ldy;
     int M, N, K;
+    int gelu;  // 1: y = gelu(g) for plain products
 };
 
 constexpr int T64 = 64, KB = 16;
@@ -76,7 +77,7 @@ __global__ __launch_bounds__(256) void f32_kernel(F32Params p) {
             if (m >= p.M) continue;
             float g = acc0[i][j];
             if (BIAS) g += p.b0[n];
-            float y = g;
+            float y = p.gelu ? 0.5f * g * (1.f + erff(g * 0.70710678118654752f)) : g;
             if (SWIGLU) {
                 float u = acc1[i][j];
                 if (BIAS) u += p.b1[n];
@@ -98,6 +99,7 @@ tp_status_t launch_f32(const LinearDesc& d, hipStream_t stream) {
     p.b0 = static_cast<const float*>(d.b0);
     p.b1 = static_cast<const float*>(d.b1);
     p.Y = static_cast<float*>(d.Y);
+    p.gelu = d.gelu ? 1 : 0;
     p.ldy = d.ldy;
     p.M = (int)d.M;
     p.N = (int)d.N;

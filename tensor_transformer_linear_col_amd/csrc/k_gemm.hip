@@ -78,9 +78,10 @@ __device__ __forceinline__ void tile_of(int b, int tiles_n, int tiles_m, int& tn
     tile_coords(xcd_major(b, tiles_n * tiles_m), tiles_n, tiles_m, tn, tm);
 }
 
-template <int TN, int TM, int WAVES_N, int WAVES_M, bool SWIGLU, bool BIAS, bool KTAIL, typename OutT>
+template <int TN, int TM, int WAVES_N, int WAVES_M, int ACT, bool BIAS, bool KTAIL, typename OutT>
 __global__ __launch_bounds__(WAVES_N* WAVES_M * 64)
 __attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_kernel(GemmParams p) {
+    constexpr bool SWIGLU = ACT == kActSwiglu;
     constexpr int NT = WAVES_N * WAVES_M * 64;
     constexpr int WN = TN / WAVES_N;           // output features per wave
     constexpr int WM = TM / WAVES_M;           // tokens per wave
@@ -232,7 +233,7 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_kernel(GemmParams p) {
                 }
                 const int n_base = n0 + wn * WN + i * 32 + 8 * q + 4 * lh;
                 const int m = m0 + wm * WM + j * 32 + l32;
-                epilogue4<SWIGLU, BIAS, OutT>(p.o, n_base, m, gv, uv);
+                epilogue4<ACT, BIAS, OutT>(p.o, n_base, m, gv, uv);
                 __builtin_amdgcn_sched_barrier(0);  // keep bias loads next to their use
             }
 }
@@ -304,8 +305,9 @@ __device__ __forceinline__ void dma_rows(const void* base, uint32_t bytes, const
 // Workgroups that run side by side on one XCD hold neighbouring tiles at the same K
 // range, so their panels are shared in that XCD's L2 (a stream-K split, whose
 // workgroups sit at different K offsets, forfeits that sharing).
-template <int TN, int TM, int WAVES_N, int WAVES_M, bool SWIGLU, bool BIAS, bool SK, typename OutT>
+template <int TN, int TM, int WAVES_N, int WAVES_M, int ACT, bool BIAS, bool SK, typename OutT>
 __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void gemm_dtl_kernel(GemmParams p) {
+    constexpr bool SWIGLU = ACT == kActSwiglu;
     constexpr int NWAVES = WAVES_N * WAVES_M;
     constexpr int NT = NWAVES * 64;
     constexpr int WN = TN / WAVES_N, WM = TM / WAVES_M;
@@ -504,7 +506,7 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void gemm_dtl_kernel(GemmPar
                         }
                         const int nl = wn * WN + i * 32 + 8 * q + 4 * lh;
                         const int ml = wm * WM + j * 32 + l32;
-                        epilogue_vals4<SWIGLU, BIAS>(p.o, n0 + nl, gv, uv, y);
+                        epilogue_vals4<ACT, BIAS>(p.o, n0 + nl, gv, uv, y);
                         const bf16x4 v = {(bf16)y[0], (bf16)y[1], (bf16)y[2], (bf16)y[3]};
                         *reinterpret_cast<bf16x4*>(lds_raw + ml * OPITCH + nl * 2) = v;
                     }
@@ -546,7 +548,7 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void gemm_dtl_kernel(GemmPar
                     }
                     const int n_base = n0 + wn * WN + i * 32 + 8 * q + 4 * lh;
                     const int m = m0 + wm * WM + j * 32 + l32;
-                    epilogue4<SWIGLU, BIAS, OutT>(p.o, n_base, m, gv, uv);
+                    epilogue4<ACT, BIAS, OutT>(p.o, n_base, m, gv, uv);
                     __builtin_amdgcn_sched_barrier(0);
                 }
     };
@@ -594,8 +596,9 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void gemm_dtl_kernel(GemmPar
 // The S pieces of each split tile, summed in K order, then the tile's epilogue.
 // Workgroup (r, i) takes block row i of split tile r with the thread layout of the
 // GEMM kernel, so thread tid reads exactly the float4 groups it would have held.
-template <int TN, int TM, int WAVES_N, int WAVES_M, bool SWIGLU, bool BIAS, typename OutT>
+template <int TN, int TM, int WAVES_N, int WAVES_M, int ACT, bool BIAS, typename OutT>
 __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void splitk_reduce_kernel(GemmParams p) {
+    constexpr bool SWIGLU = ACT == kActSwiglu;
     constexpr int NWAVES = WAVES_N * WAVES_M, NT = NWAVES * 64;
     constexpr int WN = TN / WAVES_N, WM = TM / WAVES_M;
     constexpr int BN = WN / 32, BM = WM / 32;
@@ -634,12 +637,12 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void splitk_reduce_kernel(Ge
             }
             const int n_base = tn * TN + wn * WN + i * 32 + 8 * qq + 4 * lh;
             const int m = tm * TM + wm * WM + j * 32 + l32;
-            epilogue4<SWIGLU, BIAS, OutT>(p.o, n_base, m, gv, uv);
+            epilogue4<ACT, BIAS, OutT>(p.o, n_base, m, gv, uv);
         }
     }
 }
 
-template <int TN, int TM, int WAVES_N, int WAVES_M, bool SWIGLU, bool BIAS, typename OutT>
+template <int TN, int TM, int WAVES_N, int WAVES_M, int ACT, bool BIAS, typename OutT>
 tp_status_t run_dtl(const LinearDesc& d, int cus, hipStream_t stream) {
     GemmParams p;
     p.X = static_cast<const bf16*>(d.X);
@@ -681,38 +684,38 @@ tp_status_t run_dtl(const LinearDesc& d, int cus, hipStream_t stream) {
         }
     }
     if (S == 1) {
-        hipLaunchKernelGGL((gemm_dtl_kernel<TN, TM, WAVES_N, WAVES_M, SWIGLU, BIAS, false, OutT>), dim3((unsigned)tiles),
+        hipLaunchKernelGGL((gemm_dtl_kernel<TN, TM, WAVES_N, WAVES_M, ACT, BIAS, false, OutT>), dim3((unsigned)tiles),
                            dim3(NT), 0, stream, p);
         return hip_status();
     }
-    constexpr int64_t TILEF = (int64_t)TN * (SWIGLU ? 2 : 1) * TM;  // floats of a partial tile
+    constexpr int64_t TILEF = (int64_t)TN * (ACT == kActSwiglu ? 2 : 1) * TM;  // floats of a partial tile
     p.F = (int)F;
     p.S = S;
     Workspace ws;
     tp_status_t st = get_workspace(stream, (size_t)(R * S * TILEF), 0, &ws);
     if (st != TP_OK) return st;
     p.ws = ws.partials;
-    hipLaunchKernelGGL((gemm_dtl_kernel<TN, TM, WAVES_N, WAVES_M, SWIGLU, BIAS, true, OutT>),
+    hipLaunchKernelGGL((gemm_dtl_kernel<TN, TM, WAVES_N, WAVES_M, ACT, BIAS, true, OutT>),
                        dim3((unsigned)(F + R * S)), dim3(NT), 0, stream, p);
     st = hip_status();
     if (st != TP_OK) return st;
     constexpr int BN = TN / WAVES_N / 32;
-    hipLaunchKernelGGL((splitk_reduce_kernel<TN, TM, WAVES_N, WAVES_M, SWIGLU, BIAS, OutT>), dim3((unsigned)(R * BN)),
+    hipLaunchKernelGGL((splitk_reduce_kernel<TN, TM, WAVES_N, WAVES_M, ACT, BIAS, OutT>), dim3((unsigned)(R * BN)),
                        dim3(NT), 0, stream, p);
     return hip_status();
 }
 
-template <int TN, int TM, int WAVES_N, int WAVES_M, bool SWIGLU>
+template <int TN, int TM, int WAVES_N, int WAVES_M, int ACT>
 tp_status_t run_dtl_bias(const LinearDesc& d, int cus, hipStream_t stream) {
     const bool bias = d.b0 != nullptr;
     if (d.out_dtype == TP_DTYPE_BF16)
-        return bias ? run_dtl<TN, TM, WAVES_N, WAVES_M, SWIGLU, true, bf16>(d, cus, stream)
-                    : run_dtl<TN, TM, WAVES_N, WAVES_M, SWIGLU, false, bf16>(d, cus, stream);
-    return bias ? run_dtl<TN, TM, WAVES_N, WAVES_M, SWIGLU, true, float>(d, cus, stream)
-                : run_dtl<TN, TM, WAVES_N, WAVES_M, SWIGLU, false, float>(d, cus, stream);
+        return bias ? run_dtl<TN, TM, WAVES_N, WAVES_M, ACT, true, bf16>(d, cus, stream)
+                    : run_dtl<TN, TM, WAVES_N, WAVES_M, ACT, false, bf16>(d, cus, stream);
+    return bias ? run_dtl<TN, TM, WAVES_N, WAVES_M, ACT, true, float>(d, cus, stream)
+                : run_dtl<TN, TM, WAVES_N, WAVES_M, ACT, false, float>(d, cus, stream);
 }
 
-template <int TN, int TM, int WAVES_N, int WAVES_M, bool SWIGLU, bool BIAS, bool KTAIL, typename OutT>
+template <int TN, int TM, int WAVES_N, int WAVES_M, int ACT, bool BIAS, bool KTAIL, typename OutT>
 tp_status_t run(const LinearDesc& d, hipStream_t stream) {
     GemmParams p;
     p.X = static_cast<const bf16*>(d.X);
@@ -733,26 +736,26 @@ tp_status_t run(const LinearDesc& d, hipStream_t stream) {
     p.tiles_n = (int)ceil_div(d.N, TN);
     p.tiles_m = (int)ceil_div(d.M, TM);
     const int64_t tiles = (int64_t)p.tiles_n * p.tiles_m;
-    hipLaunchKernelGGL((gemm_kernel<TN, TM, WAVES_N, WAVES_M, SWIGLU, BIAS, KTAIL, OutT>), dim3((unsigned)tiles),
+    hipLaunchKernelGGL((gemm_kernel<TN, TM, WAVES_N, WAVES_M, ACT, BIAS, KTAIL, OutT>), dim3((unsigned)tiles),
                        dim3(WAVES_N * WAVES_M * 64), 0, stream, p);
     return hip_status();
 }
 
-template <int TN, int TM, int WAVES_N, int WAVES_M, bool SWIGLU, bool BIAS, bool KTAIL>
+template <int TN, int TM, int WAVES_N, int WAVES_M, int ACT, bool BIAS, bool KTAIL>
 tp_status_t run_out(const LinearDesc& d, hipStream_t stream) {
-    return d.out_dtype == TP_DTYPE_BF16 ? run<TN, TM, WAVES_N, WAVES_M, SWIGLU, BIAS, KTAIL, bf16>(d, stream)
-                                        : run<TN, TM, WAVES_N, WAVES_M, SWIGLU, BIAS, KTAIL, float>(d, stream);
+    return d.out_dtype == TP_DTYPE_BF16 ? run<TN, TM, WAVES_N, WAVES_M, ACT, BIAS, KTAIL, bf16>(d, stream)
+                                        : run<TN, TM, WAVES_N, WAVES_M, ACT, BIAS, KTAIL, float>(d, stream);
 }
 
-template <int TN, int TM, int WAVES_N, int WAVES_M, bool SWIGLU>
+template <int TN, int TM, int WAVES_N, int WAVES_M, int ACT>
 tp_status_t run_bias(const LinearDesc& d, hipStream_t stream) {
     const bool bias = d.b0 != nullptr;
     const bool ktail = d.K % BK != 0;
     if (bias)
-        return ktail ? run_out<TN, TM, WAVES_N, WAVES_M, SWIGLU, true, true>(d, stream)
-                     : run_out<TN, TM, WAVES_N, WAVES_M, SWIGLU, true, false>(d, stream);
-    return ktail ? run_out<TN, TM, WAVES_N, WAVES_M, SWIGLU, false, true>(d, stream)
-                 : run_out<TN, TM, WAVES_N, WAVES_M, SWIGLU, false, false>(d, stream);
+        return ktail ? run_out<TN, TM, WAVES_N, WAVES_M, ACT, true, true>(d, stream)
+                     : run_out<TN, TM, WAVES_N, WAVES_M, ACT, true, false>(d, stream);
+    return ktail ? run_out<TN, TM, WAVES_N, WAVES_M, ACT, false, true>(d, stream)
+                 : run_out<TN, TM, WAVES_N, WAVES_M, ACT, false, false>(d, stream);
 }
 
 }  // namespace
@@ -778,15 +781,19 @@ tp_status_t launch_gemm(const LinearDesc& d, hipStream_t stream) {
     if (d.swiglu) {
         const int64_t big = ceil_div(d.N, 128) * ceil_div(d.M, 256);
         if (dma && (big >= cus || big * kt >= 16 * (int64_t)cus))
-            return run_dtl_bias<128, 256, 2, TP_DMA_WAVES_M, true>(d, cus, stream);
-        if (big >= cus) return run_bias<128, 256, 2, 2, true>(d, stream);
-        return run_bias<64, 128, 2, 2, true>(d, stream);
+            return run_dtl_bias<128, 256, 2, TP_DMA_WAVES_M, kActSwiglu>(d, cus, stream);
+        if (big >= cus) return run_bias<128, 256, 2, 2, kActSwiglu>(d, stream);
+        return run_bias<64, 128, 2, 2, kActSwiglu>(d, stream);
     }
     const int64_t big = ceil_div(d.N, 256) * ceil_div(d.M, 256);
-    if (dma && (big >= cus || big * kt >= 16 * (int64_t)cus))
-        return run_dtl_bias<256, 256, 2, TP_DMA_WAVES_M, false>(d, cus, stream);
-    if (big >= cus) return run_bias<256, 256, 2, 2, false>(d, stream);
-    return run_bias<128, 128, 2, 2, false>(d, stream);
+    auto plain = [&](auto act) -> tp_status_t {
+        constexpr int A = decltype(act)::value;
+        if (dma && (big >= cus || big * kt >= 16 * (int64_t)cus))
+            return run_dtl_bias<256, 256, 2, TP_DMA_WAVES_M, A>(d, cus, stream);
+        if (big >= cus) return run_bias<256, 256, 2, 2, A>(d, stream);
+        return run_bias<128, 128, 2, 2, A>(d, stream);
+    };
+    return d.gelu ? plain(std::integral_constant<int, kActGelu>{}) : plain(std::integral_constant<int, kActNone>{});
 }
 
 }  // namespace tp

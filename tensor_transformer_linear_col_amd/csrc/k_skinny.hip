@@ -27,6 +27,7 @@
 // A and B use the same K placement, so the dot products are exact whatever order
 // the unit reduces K in.
 #include <algorithm>
+#include <type_traits>
 
 #include "tp_epilogue.h"
 
@@ -69,8 +70,9 @@ __device__ __forceinline__ bf16x8 ld8(const bf16* p) {
 // MT: 16-token tiles; RT: 16-row weight tiles per wave (SwiGLU: RT/2 gate + RT/2 up);
 // NW: waves per workgroup; U: 32-wide K steps per piece; PERSIST: ranges of many
 // units (else exactly one unit per workgroup).
-template <int MT, int RT, int NW, int U, bool PERSIST, bool SWIGLU, bool BIAS, typename OutT>
+template <int MT, int RT, int NW, int U, bool PERSIST, int ACT, bool BIAS, typename OutT>
 __global__ __launch_bounds__(NW * 64) void skinny_kernel(SkinnyParams p) {
+    constexpr bool SWIGLU = ACT == kActSwiglu;
     constexpr int RH = SWIGLU ? RT / 2 : RT;  // output row tiles
     constexpr int KS = 32 * U;                // K elements per piece
     constexpr int TILEF = RT * MT * 4 * 64;   // floats of one workgroup's partial tile
@@ -205,7 +207,7 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(SkinnyParams p) {
                 uv[e] = c;
             }
             if (whole) {
-                epilogue4<SWIGLU, BIAS, OutT>(p.o, g * 16 * RH + t * 16 + 4 * (ln >> 4), j * 16 + (ln & 15), gv, uv);
+                epilogue4<ACT, BIAS, OutT>(p.o, g * 16 * RH + t * 16 + 4 * (ln >> 4), j * 16 + (ln & 15), gv, uv);
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -255,7 +257,7 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(SkinnyParams p) {
                                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                         }
                     }
-                    epilogue4<SWIGLU, BIAS, OutT>(p.o, g * 16 * RH + t * 16 + 4 * (ln >> 4), j * 16 + (ln & 15), gv,
+                    epilogue4<ACT, BIAS, OutT>(p.o, g * 16 * RH + t * 16 + 4 * (ln >> 4), j * 16 + (ln & 15), gv,
                                                   uv);
                 }
                 if (threadIdx.x == 0)
@@ -280,9 +282,9 @@ int device_cus() {
     return cached[dev];
 }
 
-template <int MT, int RT, int NW, int U, bool PERSIST, bool SWIGLU, bool BIAS, typename OutT>
+template <int MT, int RT, int NW, int U, bool PERSIST, int ACT, bool BIAS, typename OutT>
 tp_status_t run(const LinearDesc& d, hipStream_t stream) {
-    constexpr int RH = SWIGLU ? RT / 2 : RT;
+    constexpr int RH = ACT == kActSwiglu ? RT / 2 : RT;
     constexpr int KS = 32 * U;
     constexpr int TILEF = RT * MT * 4 * 64;
     SkinnyParams p;
@@ -336,19 +338,19 @@ tp_status_t run(const LinearDesc& d, hipStream_t stream) {
         p.ws = ws.partials;
         p.counters = ws.counters;
     }
-    hipLaunchKernelGGL((skinny_kernel<MT, RT, NW, U, PERSIST, SWIGLU, BIAS, OutT>), dim3((unsigned)P),
+    hipLaunchKernelGGL((skinny_kernel<MT, RT, NW, U, PERSIST, ACT, BIAS, OutT>), dim3((unsigned)P),
                        dim3(NW * 64), 0, stream, p);
     return hip_status();
 }
 
-template <int MT, int RT, int NW, int U, bool PERSIST, bool SWIGLU>
+template <int MT, int RT, int NW, int U, bool PERSIST, int ACT>
 tp_status_t run_bias(const LinearDesc& d, hipStream_t stream) {
     const bool bias = d.b0 != nullptr;
     if (d.out_dtype == TP_DTYPE_BF16)
-        return bias ? run<MT, RT, NW, U, PERSIST, SWIGLU, true, bf16>(d, stream)
-                    : run<MT, RT, NW, U, PERSIST, SWIGLU, false, bf16>(d, stream);
-    return bias ? run<MT, RT, NW, U, PERSIST, SWIGLU, true, float>(d, stream)
-                : run<MT, RT, NW, U, PERSIST, SWIGLU, false, float>(d, stream);
+        return bias ? run<MT, RT, NW, U, PERSIST, ACT, true, bf16>(d, stream)
+                    : run<MT, RT, NW, U, PERSIST, ACT, false, bf16>(d, stream);
+    return bias ? run<MT, RT, NW, U, PERSIST, ACT, true, float>(d, stream)
+                : run<MT, RT, NW, U, PERSIST, ACT, false, float>(d, stream);
 }
 
 }  // namespace
@@ -357,20 +359,24 @@ tp_status_t launch_skinny(const LinearDesc& d, hipStream_t stream) {
     const int mt = (int)ceil_div(d.M, 16);
     if (d.swiglu) {
         switch (mt) {
-            case 1: return run_bias<1, 2, 8, TP_SKINNY_U1, false, true>(d, stream);
-            case 2: return run_bias<2, 2, 4, 2, false, true>(d, stream);
-            case 3: return run_bias<3, 2, 4, 2, false, true>(d, stream);
-            case 4: return run_bias<4, 4, 4, TP_SKINNY_U4, true, true>(d, stream);
+            case 1: return run_bias<1, 2, 8, TP_SKINNY_U1, false, kActSwiglu>(d, stream);
+            case 2: return run_bias<2, 2, 4, 2, false, kActSwiglu>(d, stream);
+            case 3: return run_bias<3, 2, 4, 2, false, kActSwiglu>(d, stream);
+            case 4: return run_bias<4, 4, 4, TP_SKINNY_U4, true, kActSwiglu>(d, stream);
             default: return TP_ERR_SHAPE;
         }
     }
-    switch (mt) {
-        case 1: return run_bias<1, 1, 8, TP_SKINNY_U1, false, false>(d, stream);
-        case 2: return run_bias<2, 2, 4, 2, false, false>(d, stream);
-        case 3: return run_bias<3, 2, 4, 2, false, false>(d, stream);
-        case 4: return run_bias<4, 4, 4, TP_SKINNY_U4, true, false>(d, stream);
-        default: return TP_ERR_SHAPE;
-    }
+    auto plain = [&](auto act) -> tp_status_t {
+        constexpr int A = decltype(act)::value;
+        switch (mt) {
+            case 1: return run_bias<1, 1, 8, TP_SKINNY_U1, false, A>(d, stream);
+            case 2: return run_bias<2, 2, 4, 2, false, A>(d, stream);
+            case 3: return run_bias<3, 2, 4, 2, false, A>(d, stream);
+            case 4: return run_bias<4, 4, 4, TP_SKINNY_U4, true, A>(d, stream);
+            default: return TP_ERR_SHAPE;
+        }
+    };
+    return d.gelu ? plain(std::integral_constant<int, kActGelu>{}) : plain(std::integral_constant<int, kActNone>{});
 }
 
 }  // namespace tp

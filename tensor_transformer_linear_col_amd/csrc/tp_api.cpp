@@ -165,6 +165,31 @@ tp_status_t tp_mlp_shard(const void* X, const void* Wg_r, const void* Wu_r, cons
     return launch_linear(down, s);
 }
 
+tp_status_t tp_ffn_gelu_shard(const void* X, const void* W1_r, const void* b1_r, const void* W2_r, void* H_r,
+                              void* P_r, int64_t M, int64_t hidden, int64_t intermediate, int32_t tp_size,
+                              tp_dtype_t dtype, tp_dtype_t partial_dtype, void* stream) {
+    if (!X || !W1_r || !H_r) return TP_ERR_NULL;
+    if (P_r && !W2_r) return TP_ERR_NULL;
+    if (!dtype_ok(dtype) || !dtype_ok(partial_dtype)) return TP_ERR_DTYPE;
+    if (dtype == TP_DTYPE_F32 && partial_dtype != TP_DTYPE_F32) return TP_ERR_DTYPE;
+    TP_TRY(check_dims(M, {hidden, intermediate}));
+    if (tp_size < 1 || tp_size > kMaxTP) return TP_ERR_SHAPE;
+    if (intermediate % tp_size != 0) return TP_ERR_INDIVISIBLE;
+    const int64_t i = intermediate / tp_size;
+    TP_TRY(check_vec_operand(X, hidden, dtype));
+    TP_TRY(check_vec_operand(W1_r, hidden, dtype));
+    if (P_r) {
+        TP_TRY(check_vec_operand(H_r, i, dtype));
+        TP_TRY(check_vec_operand(W2_r, i, dtype));
+    }
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    LinearDesc up{X, hidden, W1_r, nullptr, b1_r, nullptr, H_r, i, M, i, hidden, dtype, dtype, false, true};
+    TP_TRY(launch_linear(up, s));
+    if (!P_r) return TP_OK;
+    LinearDesc down{H_r, i, W2_r, nullptr, nullptr, nullptr, P_r, hidden, M, hidden, i, dtype, partial_dtype, false};
+    return launch_linear(down, s);
+}
+
 tp_status_t tp_attn_proj_shard(const void* X, const void* Wqkv_r, const void* bqkv_r, void* QKV_r, const void* A_r,
                                const void* Wo_r, void* P_r, int64_t M, int64_t hidden, int32_t n_heads,
                                int32_t n_kv_heads, int32_t head_dim, int32_t tp_size, tp_dtype_t dtype,

@@ -42,12 +42,22 @@ __device__ __forceinline__ void store_out4<float>(float* row, int n_base, int N,
     }
 }
 
+// gelu(z) = z * Phi(z) = z * (1 + erf(z / sqrt(2))) / 2, the exact form the pages'
+// FFN applies ("Understanding Tensor Parallelism for Multi-GPU LLM Serving",
+// section "Implementing Tensor Parallelism with Hugging Face Accelerate").
+__device__ __forceinline__ float gelu_erf(float z) { return 0.5f * z * (1.f + erff(z * 0.70710678118654752f)); }
+
+// Output activation of a product, a compile-time choice of every kernel.
+enum : int { kActNone = 0, kActSwiglu = 1, kActGelu = 2 };
+
 // Four consecutive outputs n_base..n_base+3 from fp32 sums g (and u):
-//   plain:  y = g + b0[n]
+//   none:   y = g + b0[n]
+//   GELU:   y = gelu(g + b0[n])
 //   SwiGLU: y = silu(g + b0[n]) * (u + b1[n]),  silu(z) = z / (1 + exp(-z))
-template <bool SWIGLU, bool BIAS>
+template <int ACT, bool BIAS>
 __device__ __forceinline__ void epilogue_vals4(const OutDesc& o, int n_base, const float g[4], const float u[4],
                                                float y[4]) {
+    constexpr bool SWIGLU = ACT == kActSwiglu;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int n = n_base + e;
@@ -57,16 +67,16 @@ __device__ __forceinline__ void epilogue_vals4(const OutDesc& o, int n_base, con
             a += (float)o.b0[n];
             if (SWIGLU) c += (float)o.b1[n];
         }
-        y[e] = SWIGLU ? a / (1.f + expf(-a)) * c : a;
+        y[e] = SWIGLU ? a / (1.f + expf(-a)) * c : (ACT == kActGelu ? gelu_erf(a) : a);
     }
 }
 
 // The same four outputs of token row m, rounded once to OutT and stored.
-template <bool SWIGLU, bool BIAS, typename OutT>
+template <int ACT, bool BIAS, typename OutT>
 __device__ __forceinline__ void epilogue4(const OutDesc& o, int n_base, int m, const float g[4], const float u[4]) {
     if (m >= o.M) return;
     float y[4];
-    epilogue_vals4<SWIGLU, BIAS>(o, n_base, g, u, y);
+    epilogue_vals4<ACT, BIAS>(o, n_base, g, u, y);
     OutT* row = reinterpret_cast<OutT*>(o.Y) + (int64_t)m * o.ldy;
     store_out4<OutT>(row, n_base, o.N, y, o.vec_store != 0);
 }

@@ -29,6 +29,7 @@ struct LinearDesc {
     tp_dtype_t in_dtype;   // dtype of X, W, b
     tp_dtype_t out_dtype;  // dtype of Y
     bool swiglu;
+    bool gelu = false;  // plain products only: y = gelu(XW^T + b), erf form
 };
 
 // Split-K work space: fp32 partial tiles and per-tile arrival counters.

@@ -31,7 +31,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     for name in names:
         assert hasattr(L, name), name
     assert set(names) == set(tp.EXPORTS)
@@ -97,6 +97,23 @@ def test_mlp_shard_errors(L):
     assert mlp(L, dt=F32, pdt=BF16) == DTYPE
     assert mlp(L, M=0) == OK
     assert mlp(L, M=0, Wd=0, Pr=0) == OK             # down projection skipped
+
+
+def gelu_ffn(L, X=P, W1=P, b1=0, W2=P, H=P, Pr=P, M=4, h=4096, i=11008, p=2, dt=BF16, pdt=BF16):
+    return L.tp_ffn_gelu_shard(X, W1, b1, W2, H, Pr, M, h, i, p, dt, pdt, None)
+
+
+def test_ffn_gelu_shard_errors(L):
+    assert gelu_ffn(L, X=0) == NULL
+    assert gelu_ffn(L, W1=0) == NULL
+    assert gelu_ffn(L, H=0) == NULL
+    assert gelu_ffn(L, W2=0) == NULL                 # the row layer needs its weights
+    assert gelu_ffn(L, i=11008, p=3) == INDIV        # the listing's divisibility assert
+    assert gelu_ffn(L, p=0) == SHAPE
+    assert gelu_ffn(L, W1=P + 2) == ALIGN
+    assert gelu_ffn(L, dt=F32, pdt=BF16) == DTYPE
+    assert gelu_ffn(L, M=0) == OK
+    assert gelu_ffn(L, M=0, W2=0, Pr=0) == OK        # row layer skipped
 
 
 def attn(L, X=P, Wqkv=P, b=0, QKV=P, A=P, Wo=P, Pr=P, M=1, h=8192, nh=64, nkv=8, d=128, p=8,
