@@ -42,6 +42,10 @@ Parity status per function (what pins it, beside itself):
       normal CDF values); the FFN by the sharded-equals-unsharded invariant.
   qkv head layout / attention stand-in (A := Q):  parity unpinned by the
       pages (self-consistency invariants only).
+  kv_heads_of with more shards than KV heads (replication):  a reading,
+      parity unpinned by the pages (self-consistency invariants only).
+  blocks_of / row_shard_uneven:  pinned by the uneven-split invariant of [P5]
+      "Try it yourself" and brute force.
 """
 from __future__ import annotations
 
@@ -126,6 +130,30 @@ def col_shard_uneven(w, b, widths):
     if start != np.shape(w)[0]:
         raise ValueError("widths do not cover the output features")
     return out
+
+
+def blocks_of(n: int, widths):
+    """Consecutive blocks of the given widths covering n ([P5] "Try it yourself": an uneven
+    split still matches exactly)."""
+    out, start = [], 0
+    for width in widths:
+        if width <= 0:
+            raise ValueError("block widths must be positive")
+        out.append(slice(start, start + width))
+        start += width
+    if start != n:
+        raise ValueError("widths do not cover the dimension")
+    return out
+
+
+def row_shard_uneven(w, widths):
+    """Row split into consecutive input-column blocks of the given widths."""
+    return [f64(w)[:, s] for s in blocks_of(np.shape(w)[1], widths)]
+
+
+def input_slices_uneven(x, widths):
+    """The matching column blocks of the row layer's input."""
+    return [f64(x)[:, s] for s in blocks_of(np.shape(x)[1], widths)]
 
 
 def row_shard(w, p: int, r: int) -> np.ndarray:
@@ -279,17 +307,30 @@ def ffn_gelu_shards(x, w1, w2, p, b1=None):
 # attention block)
 # ---------------------------------------------------------------------------
 
+def kv_heads_of(n_kv_heads, p, r):
+    """KV heads held by shard r: the block [r*G/p, (r+1)*G/p) when p divides G. When there
+    are more shards than KV heads and p is a multiple of G (a reading: the pages only say
+    the TP size divides the heads), each KV head is replicated on p/G consecutive shards
+    and shard r holds head floor(r*G/p)."""
+    if not 0 <= r < p:
+        raise ValueError(f"rank {r} outside [0, {p})")
+    if n_kv_heads % p == 0:
+        hk = n_kv_heads // p
+        return list(range(r * hk, (r + 1) * hk))
+    if p % n_kv_heads == 0:
+        return [r * n_kv_heads // p]
+    raise ValueError("tensor_parallel_size must divide the KV heads or be a multiple of them")
+
+
 def qkv_rows(n_heads, n_kv_heads, head_dim, p, r):
     """Row indices of the fused [Wq; Wk; Wv] weight owned by shard r, in order Q | K | V."""
-    if n_heads % p or n_kv_heads % p:
+    if n_heads % p:
         raise ValueError("tensor_parallel_size must divide the head counts")
-    hq, hk = n_heads // p, n_kv_heads // p
-    d = head_dim
+    hq, d = n_heads // p, head_dim
     q = np.arange(r * hq * d, (r + 1) * hq * d)
-    k0 = n_heads * d
-    k = np.arange(k0 + r * hk * d, k0 + (r + 1) * hk * d)
-    v0 = (n_heads + n_kv_heads) * d
-    v = np.arange(v0 + r * hk * d, v0 + (r + 1) * hk * d)
+    kv = kv_heads_of(n_kv_heads, p, r)
+    k = np.concatenate([np.arange((n_heads + h) * d, (n_heads + h + 1) * d) for h in kv])
+    v = np.concatenate([np.arange((n_heads + n_kv_heads + h) * d, (n_heads + n_kv_heads + h + 1) * d) for h in kv])
     return np.concatenate([q, k, v])
 
 

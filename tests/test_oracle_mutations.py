@@ -87,6 +87,13 @@ def _qkv_rows_shared_kv(n_heads, n_kv_heads, head_dim, p, r):
     return np.concatenate([q, k, v])
 
 
+def _kv_heads_of_no_replication(n_kv_heads, p, r):
+    if n_kv_heads % p == 0:
+        hk = n_kv_heads // p
+        return list(range(r * hk, (r + 1) * hk))
+    return [r % n_kv_heads]          # round-robin instead of consecutive blocks
+
+
 MUTATIONS = [
     ("linear", _linear_no_bias, [P.test_toy_full_output_matches_printed_values]),
     ("linear", _linear_bias_twice, [P.test_toy_full_output_matches_printed_values,
@@ -101,6 +108,7 @@ MUTATIONS = [
     ("row_shard", _row_shard_wrong_axis, [P.test_toy_row_split_sum_plus_bias_equals_unsharded]),
     ("concat", _concat_reversed, [P.test_toy_column_split_concat_matches_printed_values_and_is_exact]),
     ("qkv_rows", _qkv_rows_shared_kv, [P.test_qkv_head_split_concat_and_one_hot]),
+    ("kv_heads_of", _kv_heads_of_no_replication, [P.test_kv_heads_replicated_when_more_shards_than_kv_heads]),
 ]
 
 

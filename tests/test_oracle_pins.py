@@ -196,6 +196,46 @@ def test_uneven_split_9_equals_5_plus_4():
     np.testing.assert_array_equal(O.concat(parts), O.linear(x, w, b))
 
 
+def test_uneven_row_split_sum_equals_unsharded():
+    """The row layer split unevenly (5 + 3 + 8 inputs): the partials still sum to X W^T."""
+    x = I.as_numpy_f64(I.activations(3, 16, seed=51))
+    w = I.as_numpy_f64(I.weight(7, 16, seed=52))
+    widths = (5, 3, 8)
+    parts = [O.row_partial(x_r, w_r) for x_r, w_r in zip(O.input_slices_uneven(x, widths), O.row_shard_uneven(w, widths))]
+    np.testing.assert_allclose(O.combine_sum(parts), O.linear(x, w), rtol=1e-13, atol=1e-15)
+    # brute force on every entry
+    ref = O.linear_fsum(x, w)
+    np.testing.assert_allclose(O.combine_sum(parts), ref, rtol=1e-13, atol=1e-15)
+    with pytest.raises(ValueError):
+        O.row_shard_uneven(w, (5, 3, 7))
+    with pytest.raises(ValueError):
+        O.blocks_of(16, (16, 0))
+
+
+def test_kv_heads_replicated_when_more_shards_than_kv_heads():
+    """A reading (the pages only require TP to divide the heads): with p a multiple of the
+    KV head count, KV head h lives on the p/G consecutive shards h*p/G .. (h+1)*p/G - 1."""
+    assert [O.kv_heads_of(8, 16, r) for r in range(16)] == [[r // 2] for r in range(16)]
+    assert [O.kv_heads_of(8, 4, r) for r in range(4)] == [[2 * r, 2 * r + 1] for r in range(4)]
+    assert O.kv_heads_of(2, 8, 7) == [1]
+    with pytest.raises(ValueError):
+        O.kv_heads_of(8, 12, 0)
+    nh, nkv, d, hid, p = 8, 2, 4, 16, 4
+    shape = I.LayerShape("t", hidden=hid, n_heads=nh, n_kv_heads=nkv, head_dim=d, tp=p, seed=12)
+    wt = {k: I.as_numpy_f64(v) for k, v in I.attn_weights(shape).items()}
+    x = I.as_numpy_f64(I.activations(3, hid, seed=121))
+    full = O.linear(x, wt["Wqkv"], wt["bqkv"])
+    hq = nh // p
+    for r in range(p):
+        w_r, b_r = O.qkv_shard(wt["Wqkv"], wt["bqkv"], nh, nkv, d, p, r)
+        assert w_r.shape == ((hq + 2) * d, hid)
+        y = O.col_linear(x, w_r, b_r)
+        h = r * nkv // p
+        np.testing.assert_array_equal(y[:, :hq * d], full[:, r * hq * d:(r + 1) * hq * d])
+        np.testing.assert_array_equal(y[:, hq * d:(hq + 1) * d], full[:, (nh + h) * d:(nh + h + 1) * d])
+        np.testing.assert_array_equal(y[:, (hq + 1) * d:], full[:, (nh + nkv + h) * d:(nh + nkv + h + 1) * d])
+
+
 def test_indivisible_sizes_are_rejected():
     w = np.zeros((10, 9))
     with pytest.raises(ValueError):
