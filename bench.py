@@ -267,7 +267,72 @@ def decode_bench(iters=30):
         log(f"decode {shape.name} M={M}: column+gelu {cu*1e3:.1f} us, row {rw*1e3:.1f} us")
     del sets, base
     torch.cuda.empty_cache()
+    results += split_variants_bench(iters)
     return results
+
+
+def _median_launch_us(fn, n_sets, iters):
+    import torch
+    hold_gpu(5e-3)
+    evs = []
+    for it in range(iters):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn(it % n_sets)
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) for a, b in evs)[len(evs) // 2] * 1e3
+
+
+def split_variants_bench(iters=30):
+    """Decode shards of the two split variants: an uneven column split (the 7B FFN's 11008
+    gate rows over 3 shards, 3672 + 3672 + 3664, which the listing's divisibility assert would
+    reject) and a QKV shard with KV-head replication (70B attention at TP = 16: 4 Q heads and
+    one of the 8 KV heads per shard). Weights rotated through > 1 GiB; M = 1."""
+    import torch
+    import tensor_transformer_linear_col_amd as tp
+    import tp_inputs as I
+    BF = torch.bfloat16
+    out = []
+    # uneven column split, shard 0 (the widest)
+    h, width = 4096, 3672
+    w = I.weight(width, h, seed=901).cuda()
+    copies = 1 + (1 << 30) // (width * h * 2)
+    sets = [w] + [w.clone() for _ in range(copies - 1)]
+    x = I.activations(1, h, seed=902).cuda()
+    y = torch.empty(1, width, dtype=BF, device="cuda")
+    fn = lambda c: tp.tp_linear_col(x, sets[c], None, y, 1, h, width, 1)
+    for c in range(len(sets)):
+        fn(c)
+    torch.cuda.synchronize()
+    us = _median_launch_us(fn, len(sets), iters)
+    by = width * h * 2 + h * 2 + width * 2
+    out.append({"workload": "llama7b-ffn-uneven-tp3 (shard 0 of 3672/3672/3664)", "M": 1, "op": "col",
+                "us": round(us, 2), "GB_s": round(by / us / 1e3, 1), "hbm_frac": round(by / us / 1e3 / HBM_PEAK_GBS, 3),
+                "TFLOP_s": round(2.0 * width * h / us / 1e6, 3)})
+    del sets, w
+    # QKV shard with KV-head replication
+    nh, nkv, d, hid, p = 64, 8, 128, 8192, 16
+    nq = (nh // p + 2) * d
+    wq = I.weight(nq, hid, seed=903).cuda()
+    copies = 1 + (1 << 30) // (nq * hid * 2)
+    sets = [wq] + [wq.clone() for _ in range(copies - 1)]
+    x = I.activations(1, hid, seed=904).cuda()
+    q = torch.empty(1, nq, dtype=BF, device="cuda")
+    fn = lambda c: tp.tp_attn_proj_shard(x, sets[c], None, q, None, None, None, 1, hid, nh, nkv, d, p)
+    for c in range(len(sets)):
+        fn(c)
+    torch.cuda.synchronize()
+    us = _median_launch_us(fn, len(sets), iters)
+    by = nq * hid * 2 + hid * 2 + nq * 2
+    out.append({"workload": "llama70b-qkv-tp16-kv-replicated", "M": 1, "op": "qkv",
+                "us": round(us, 2), "GB_s": round(by / us / 1e3, 1), "hbm_frac": round(by / us / 1e3 / HBM_PEAK_GBS, 3),
+                "TFLOP_s": round(2.0 * nq * hid / us / 1e6, 3)})
+    del sets, wq
+    torch.cuda.empty_cache()
+    log(f"decode split variants: " + ", ".join(f"{r['workload']} {r['us']} us" for r in out))
+    return out
 
 
 # ----------------------------------------------------------------------------------------

@@ -132,7 +132,8 @@ tp_status_t tp_ffn_gelu_shard(const void* X, const void* W1_r, const void* b1_r,
  *       A_r : [M, Hq/p*d], the shard's attention output (its own heads).
  *       Wo_r : [hidden, Hq/p*d], the O projection's input-column block of those heads.
  *   Hq = n_heads, G = n_kv_heads, d = head_dim; bqkv_r may be NULL.
- * TP_ERR_INDIVISIBLE if n_heads % tp_size or n_kv_heads % tp_size != 0. */
+ * TP_ERR_INDIVISIBLE if n_heads % tp_size != 0, or tp_size neither divides n_kv_heads nor is a
+ * multiple of it (then each KV head is replicated, as for tp_shard_qkv). */
 tp_status_t tp_attn_proj_shard(const void* X, const void* Wqkv_r, const void* bqkv_r, void* QKV_r,
                                const void* A_r, const void* Wo_r, void* P_r,
                                int64_t M, int64_t hidden, int32_t n_heads, int32_t n_kv_heads,
@@ -172,7 +173,26 @@ tp_status_t tp_shard_weight(const void* W, int64_t out_features, int64_t in_feat
 
 /* Take shard `rank` of a fused [Wq; Wk; Wv] weight ([(Hq + 2G)*d, in_features]) or, with
  * in_features = 1, of its bias: the rows of Q heads r*Hq/p.., K heads r*G/p.., V heads
- * r*G/p.., in that order -> [(Hq/p + 2G/p)*d, in_features]. */
+ * r*G/p.., in that order -> [(Hq/p + 2G/p)*d, in_features]. With more shards than KV heads
+ * (tp_size a multiple of G) each KV head is replicated on p/G consecutive shards: shard r
+ * holds KV head floor(r*G/p) and its shard is [(Hq/p + 2)*d, in_features]; the same rule
+ * holds for tp_attn_proj_shard. TP_ERR_INDIVISIBLE if p does not divide Hq, or neither
+ * divides G nor is a multiple of it. */
+/* An uneven split ([P5] "Try it yourself": 9 outputs split 5 + 4 still match exactly): take
+ * the block [start, start + width) of W along axis 0 (output rows -> [width, in]) or axis 1
+ * (input columns -> [out, width]) into a contiguous buffer. The linear entry points then run
+ * the shard with tp_size = 1 and its own width (a row shard reads X + start with ldx = in).
+ * TP_ERR_SHAPE if the block leaves W or width <= 0. Exact copy. */
+tp_status_t tp_shard_weight_block(const void* W, int64_t out_features, int64_t in_features,
+                                  int32_t axis, int64_t start, int64_t width, void* W_r,
+                                  tp_dtype_t dtype, void* stream);
+
+/* Concat of an uneven column split: Y[M, sum(widths)] = [shard_0 | shard_1 | ...] with
+ * shard r of width widths[r] (host array of n_shards widths; shards: host array of device
+ * pointers, each [M, widths[r]]). Pure copy, exact. */
+tp_status_t tp_combine_concat_v(const void* const* shards, int32_t n_shards, const int64_t* widths,
+                                void* Y, int64_t M, tp_dtype_t dtype, void* stream);
+
 tp_status_t tp_shard_qkv(const void* Wqkv, int64_t in_features, int32_t n_heads, int32_t n_kv_heads,
                          int32_t head_dim, int32_t tp_size, int32_t rank, void* Wqkv_r,
                          tp_dtype_t dtype, void* stream);

@@ -17,7 +17,8 @@ import torch
 __all__ = [
     "TP_DTYPE_F32", "TP_DTYPE_BF16", "TPError", "lib", "lib_path", "tp_linear_col",
     "tp_linear_row_partial", "tp_mlp_shard", "tp_ffn_gelu_shard", "tp_attn_proj_shard", "tp_combine_concat",
-    "tp_combine_sum", "tp_shard_weight", "tp_shard_qkv", "tp_release_workspaces",
+    "tp_combine_sum", "tp_shard_weight", "tp_shard_qkv", "tp_shard_weight_block", "tp_combine_concat_v",
+    "kv_heads_per_shard", "tp_release_workspaces",
     "tp_status_string", "EXPORTS",
 ]
 
@@ -40,6 +41,8 @@ _SIGS = {
     "tp_combine_sum": [ctypes.POINTER(_vp), _i32, _i32, _vp, _vp, _i64, _i64, _i32, _vp],
     "tp_shard_weight": [_vp, _i64, _i64, _i32, _i32, _i32, _vp, _i32, _vp],
     "tp_shard_qkv": [_vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp, _i32, _vp],
+    "tp_shard_weight_block": [_vp, _i64, _i64, _i32, _i64, _i64, _vp, _i32, _vp],
+    "tp_combine_concat_v": [ctypes.POINTER(_vp), _i32, ctypes.POINTER(_i64), _vp, _i64, _i32, _vp],
     "tp_release_workspaces": [],
     "tp_status_string": [_i32],
 }
@@ -108,6 +111,16 @@ def _dev(t: torch.Tensor | None, name: str, min_numel: int | None = None) -> int
 
 def _div(a: int, p: int):
     return a // p if p > 0 and a % p == 0 else None
+
+
+def kv_heads_per_shard(n_kv_heads: int, tp_size: int):
+    """KV heads one shard holds: G/p when p divides G, one (replicated) when p is a multiple
+    of G, None otherwise (the library then returns TP_ERR_INDIVISIBLE)."""
+    if tp_size <= 0 or n_kv_heads <= 0:
+        return None
+    if n_kv_heads % tp_size == 0:
+        return n_kv_heads // tp_size
+    return 1 if tp_size % n_kv_heads == 0 else None
 
 
 def tp_linear_col(X, W_r, b_r, Y_r, M: int, in_features: int, out_features: int, tp_size: int) -> None:
@@ -181,7 +194,7 @@ def tp_ffn_gelu_shard(X, W1_r, b1_r, W2_r, H_r, P_r, M: int, hidden: int, interm
 def tp_attn_proj_shard(X, Wqkv_r, bqkv_r, QKV_r, A_r, Wo_r, P_r, M: int, hidden: int, n_heads: int,
                        n_kv_heads: int, head_dim: int, tp_size: int, partial_dtype=None) -> None:
     """QKV_r = X Wqkv_r^T + bqkv_r; P_r = A_r Wo_r^T (partial). Either half may be skipped (None)."""
-    hq, hk = _div(n_heads, tp_size), _div(n_kv_heads, tp_size)
+    hq, hk = _div(n_heads, tp_size), kv_heads_per_shard(n_kv_heads, tp_size)
     need = hq is not None and hk is not None and M > 0
     nqkv = (hq + 2 * hk) * head_dim if need else 0
     ka = hq * head_dim if need else 0
@@ -230,11 +243,31 @@ def tp_shard_weight(W, out_features: int, in_features: int, tp_size: int, rank: 
 
 def tp_shard_qkv(Wqkv, in_features: int, n_heads: int, n_kv_heads: int, head_dim: int, tp_size: int,
                  rank: int, Wqkv_r) -> None:
-    """Wqkv_r = rows of the rank's Q heads, then K heads, then V heads."""
+    """Wqkv_r = rows of the rank's Q heads, then K heads, then V heads (a KV head is
+    replicated on tp_size / n_kv_heads shards when there are more shards than KV heads)."""
     rows = (n_heads + 2 * n_kv_heads) * head_dim
+    hq, hk = _div(n_heads, tp_size), kv_heads_per_shard(n_kv_heads, tp_size)
+    shard_rows = (hq + 2 * hk) * head_dim if hq is not None and hk is not None else None
     _call("tp_shard_qkv", _dev(Wqkv, "Wqkv", rows * in_features), in_features, n_heads, n_kv_heads,
-          head_dim, tp_size, rank, _dev(Wqkv_r, "Wqkv_r", (rows * in_features) // max(tp_size, 1)),
+          head_dim, tp_size, rank, _dev(Wqkv_r, "Wqkv_r", shard_rows * in_features if shard_rows else None),
           _dt(Wqkv), _stream())
+
+
+def tp_shard_weight_block(W, out_features: int, in_features: int, axis: int, start: int, width: int,
+                          W_r) -> None:
+    """W_r = W[start:start+width, :] (axis 0) or W[:, start:start+width] (axis 1), any width."""
+    n_r = (width * in_features if axis == 0 else out_features * width) if width > 0 else None
+    _call("tp_shard_weight_block", _dev(W, "W", out_features * in_features), out_features, in_features,
+          axis, start, width, _dev(W_r, "W_r", n_r), _dt(W), _stream())
+
+
+def tp_combine_concat_v(shards, widths, Y, M: int) -> None:
+    """Y = [shards[0] | shards[1] | ...] with per-shard widths (an uneven column split)."""
+    n = len(shards)
+    total = int(sum(widths))
+    ptrs = (ctypes.c_void_p * n)(*[_dev(t, f"shards[{r}]", M * int(widths[r])) for r, t in enumerate(shards)])
+    ws = (ctypes.c_int64 * n)(*[int(w) for w in widths])
+    _call("tp_combine_concat_v", ptrs, n, ws, _dev(Y, "Y", M * total), M, _dt(Y), _stream())
 
 
 def tp_release_workspaces() -> None:

@@ -57,6 +57,14 @@ std::map<std::pair<int, hipStream_t>, WsEntry> g_ws;
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// KV heads a shard holds: G/p when p divides G; one (replicated on p/G consecutive
+// shards) when p is a multiple of G; 0 (invalid) otherwise.
+int64_t kv_heads_per_shard(int64_t n_kv_heads, int64_t p) {
+    if (n_kv_heads % p == 0) return n_kv_heads / p;
+    if (p % n_kv_heads == 0) return 1;
+    return 0;
+}
+
 }  // namespace
 
 namespace tp {
@@ -200,8 +208,8 @@ tp_status_t tp_attn_proj_shard(const void* X, const void* Wqkv_r, const void* bq
     if (dtype == TP_DTYPE_F32 && partial_dtype != TP_DTYPE_F32) return TP_ERR_DTYPE;
     TP_TRY(check_dims(M, {hidden, n_heads, n_kv_heads, head_dim}));
     if (tp_size < 1 || tp_size > kMaxTP) return TP_ERR_SHAPE;
-    if (n_heads % tp_size != 0 || n_kv_heads % tp_size != 0) return TP_ERR_INDIVISIBLE;
-    const int64_t hq = n_heads / tp_size, hk = n_kv_heads / tp_size;
+    if (n_heads % tp_size != 0 || kv_heads_per_shard(n_kv_heads, tp_size) == 0) return TP_ERR_INDIVISIBLE;
+    const int64_t hq = n_heads / tp_size, hk = kv_heads_per_shard(n_kv_heads, tp_size);
     const int64_t nqkv = (hq + 2 * hk) * head_dim;
     const int64_t ka = hq * head_dim;
     if (nqkv > kMaxDim) return TP_ERR_SHAPE;
@@ -270,16 +278,59 @@ tp_status_t tp_shard_weight(const void* W, int64_t out_features, int64_t in_feat
     return launch_copy2d(src, in_features, W_r, cols, out_features, cols, es, s);
 }
 
+tp_status_t tp_shard_weight_block(const void* W, int64_t out_features, int64_t in_features, int32_t axis,
+                                  int64_t start, int64_t width, void* W_r, tp_dtype_t dtype, void* stream) {
+    if (!W || !W_r) return TP_ERR_NULL;
+    if (!dtype_ok(dtype)) return TP_ERR_DTYPE;
+    TP_TRY(check_dims(0, {out_features, in_features}));
+    if ((axis != 0 && axis != 1) || start < 0 || width <= 0) return TP_ERR_SHAPE;
+    const int64_t n = axis == 0 ? out_features : in_features;
+    if (start + width > n) return TP_ERR_SHAPE;
+    const size_t es = elem_size(dtype);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (axis == 0) {
+        const char* src = static_cast<const char*>(W) + (size_t)start * in_features * es;
+        return launch_copy2d(src, in_features, W_r, in_features, width, in_features, es, s);
+    }
+    const char* src = static_cast<const char*>(W) + (size_t)start * es;
+    return launch_copy2d(src, in_features, W_r, width, out_features, width, es, s);
+}
+
+tp_status_t tp_combine_concat_v(const void* const* shards, int32_t n_shards, const int64_t* widths, void* Y, int64_t M,
+                                tp_dtype_t dtype, void* stream) {
+    if (!shards || !widths || !Y) return TP_ERR_NULL;
+    if (!dtype_ok(dtype)) return TP_ERR_DTYPE;
+    if (n_shards < 1 || n_shards > kMaxTP || M < 0 || M > kMaxDim) return TP_ERR_SHAPE;
+    int64_t total = 0;
+    for (int32_t r = 0; r < n_shards; ++r) {
+        if (!shards[r]) return TP_ERR_NULL;
+        if (widths[r] <= 0 || widths[r] > kMaxDim) return TP_ERR_SHAPE;
+        total += widths[r];
+    }
+    if (total > kMaxDim) return TP_ERR_SHAPE;
+    if (M == 0) return TP_OK;
+    const size_t es = elem_size(dtype);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    int64_t col = 0;
+    for (int32_t r = 0; r < n_shards; ++r) {
+        TP_TRY(launch_copy2d(shards[r], widths[r], static_cast<char*>(Y) + (size_t)col * es, total, M, widths[r], es, s));
+        col += widths[r];
+    }
+    return TP_OK;
+}
+
 tp_status_t tp_shard_qkv(const void* Wqkv, int64_t in_features, int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
                          int32_t tp_size, int32_t rank, void* Wqkv_r, tp_dtype_t dtype, void* stream) {
     if (!Wqkv || !Wqkv_r) return TP_ERR_NULL;
     if (!dtype_ok(dtype)) return TP_ERR_DTYPE;
     TP_TRY(check_dims(0, {in_features, n_heads, n_kv_heads, head_dim}));
     if (tp_size < 1 || tp_size > kMaxTP || rank < 0 || rank >= tp_size) return TP_ERR_SHAPE;
-    if (n_heads % tp_size != 0 || n_kv_heads % tp_size != 0) return TP_ERR_INDIVISIBLE;
+    if (n_heads % tp_size != 0 || kv_heads_per_shard(n_kv_heads, tp_size) == 0) return TP_ERR_INDIVISIBLE;
     const size_t es = elem_size(dtype);
-    const int64_t d = head_dim, hq = n_heads / tp_size, hk = n_kv_heads / tp_size;
-    const int64_t src_rows[3] = {rank * hq * d, n_heads * d + rank * hk * d, (n_heads + n_kv_heads) * d + rank * hk * d};
+    const int64_t d = head_dim, hq = n_heads / tp_size, hk = kv_heads_per_shard(n_kv_heads, tp_size);
+    // First KV head of the shard: rank*hk when p divides G, else rank*G/p (replicated).
+    const int64_t kv0 = (n_kv_heads % tp_size == 0) ? rank * hk : (int64_t)rank * n_kv_heads / tp_size;
+    const int64_t src_rows[3] = {rank * hq * d, (n_heads + kv0) * d, (n_heads + n_kv_heads + kv0) * d};
     const int64_t nrows[3] = {hq * d, hk * d, hk * d};
     const hipStream_t s = static_cast<hipStream_t>(stream);
     int64_t dst_row = 0;

@@ -31,7 +31,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     for name in names:
         assert hasattr(L, name), name
     assert set(names) == set(tp.EXPORTS)
@@ -121,9 +121,27 @@ def attn(L, X=P, Wqkv=P, b=0, QKV=P, A=P, Wo=P, Pr=P, M=1, h=8192, nh=64, nkv=8,
     return L.tp_attn_proj_shard(X, Wqkv, b, QKV, A, Wo, Pr, M, h, nh, nkv, d, p, dt, pdt, None)
 
 
+def test_uneven_split_entry_points_errors(L):
+    blk = lambda **k: L.tp_shard_weight_block(k.get("W", P), k.get("out", 9), k.get("inn", 8), k.get("axis", 0),
+                                              k.get("start", 5), k.get("width", 4), k.get("Wr", P), k.get("dt", F32), None)
+    assert blk(W=0) == NULL
+    assert blk(start=6) == SHAPE                     # block leaves the 9 output rows
+    assert blk(width=0) == SHAPE
+    assert blk(axis=2) == SHAPE
+    assert blk(axis=1, start=8, width=1) == SHAPE
+    ptrs = (ctypes.c_void_p * 2)(P, P)
+    ws = (ctypes.c_int64 * 2)(5, 4)
+    assert L.tp_combine_concat_v(ptrs, 2, ws, P, 0, F32, None) == OK
+    assert L.tp_combine_concat_v(ptrs, 0, ws, P, 1, F32, None) == SHAPE
+    bad = (ctypes.c_int64 * 2)(5, 0)
+    assert L.tp_combine_concat_v(ptrs, 2, bad, P, 1, F32, None) == SHAPE
+    assert L.tp_combine_concat_v(ptrs, 2, ws, 0, 1, F32, None) == NULL
+
+
 def test_attn_proj_shard_errors(L):
     assert attn(L, p=3) == INDIV                     # TP size must divide the heads
-    assert attn(L, nkv=8, p=16) == INDIV             # ... the KV heads too
+    assert attn(L, nh=48, nkv=8, p=12) == INDIV      # ... and divide, or be a multiple of, the KV heads
+    assert attn(L, nkv=8, p=16, M=0) == OK           # 16 shards, 8 KV heads: each replicated twice
     assert attn(L, A=0) == NULL
     assert attn(L, QKV=0, X=0, Wqkv=0, M=0) == OK    # QKV half skipped
     assert attn(L, Pr=0, A=0, Wo=0, M=0) == OK       # O half skipped
