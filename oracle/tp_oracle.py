@@ -46,6 +46,10 @@ Parity status per function (what pins it, beside itself):
       parity unpinned by the pages (self-consistency invariants only).
   blocks_of / row_shard_uneven:  pinned by the uneven-split invariant of [P5]
       "Try it yourself" and brute force.
+  attention_core_shard:  the core is not on the pages (a reading: causal,
+      grouped-query scaled dot-product attention); pinned by closed forms of
+      softmax attention (uniform scores give the prefix mean of V, the first
+      causal row is v_0, a dominant score selects its value row) and brute force.
 """
 from __future__ import annotations
 
@@ -349,6 +353,40 @@ def attn_proj_shard(x, wqkv_r, bqkv_r, a_r, wo_r):
     qkv_r = None if wqkv_r is None else col_linear(x, wqkv_r, bqkv_r)
     p_r = None if wo_r is None else row_partial(a_r, wo_r)
     return qkv_r, p_r
+
+
+# ---------------------------------------------------------------------------
+# Head-local attention core between QKV_r and the O projection.  Heads go to
+# different GPUs ([P4] "How a layer is split"), so a shard attends with its own
+# heads only and needs no exchange.  The core itself is not on the pages; this is
+# the plain reading: scaled dot-product attention over the M tokens of one
+# sequence, causal (a decoder), grouped-query (query head h of the shard uses its
+# KV head h // (hq / hk)).
+# ---------------------------------------------------------------------------
+
+def kv_group_of(h, hq, hk):
+    """The shard-local KV head of shard-local query head h."""
+    return h // (hq // hk)
+
+
+def attention_core_shard(qkv_r, hq, hk, d, causal=True):
+    """A_r[M, hq*d] from QKV_r[M, (hq + 2 hk) d] (segments Q | K | V): for each query head h,
+    O_h = softmax(Q_h K_g^T / sqrt(d), masked to keys j <= i when causal) V_g, g = kv_group_of(h)."""
+    qkv_r = f64(qkv_r)
+    m = qkv_r.shape[0]
+    out = np.empty((m, hq * d))
+    for h in range(hq):
+        g = kv_group_of(h, hq, hk)
+        q = qkv_r[:, h * d:(h + 1) * d]
+        k = qkv_r[:, (hq + g) * d:(hq + g + 1) * d]
+        v = qkv_r[:, (hq + hk + g) * d:(hq + hk + g + 1) * d]
+        s = (q @ k.T) / math.sqrt(d)
+        if causal:
+            s = np.where(np.tril(np.ones((m, m), dtype=bool)), s, -np.inf)
+        s = s - s.max(axis=1, keepdims=True)
+        e = np.exp(s)
+        out[:, h * d:(h + 1) * d] = (e / e.sum(axis=1, keepdims=True)) @ v
+    return out
 
 
 # ---------------------------------------------------------------------------

@@ -94,6 +94,34 @@ def _kv_heads_of_no_replication(n_kv_heads, p, r):
     return [r % n_kv_heads]          # round-robin instead of consecutive blocks
 
 
+def _kv_group_round_robin(h, hq, hk):
+    return h % hk
+
+
+def _attention_unscaled(qkv_r, hq, hk, d, causal=True):
+    return _attn_variant(qkv_r, hq, hk, d, causal, 1.0, True)
+
+
+def _attention_no_mask(qkv_r, hq, hk, d, causal=True):
+    return _attn_variant(qkv_r, hq, hk, d, causal, 1.0 / np.sqrt(d), False)
+
+
+def _attn_variant(qkv_r, hq, hk, d, causal, scale, mask):
+    qkv_r = T.f64(qkv_r)
+    m = qkv_r.shape[0]
+    out = np.empty((m, hq * d))
+    for h in range(hq):
+        g = h // (hq // hk)
+        q, k = qkv_r[:, h * d:(h + 1) * d], qkv_r[:, (hq + g) * d:(hq + g + 1) * d]
+        v = qkv_r[:, (hq + hk + g) * d:(hq + hk + g + 1) * d]
+        s = (q @ k.T) * scale
+        if causal and mask:
+            s = np.where(np.tril(np.ones((m, m), dtype=bool)), s, -np.inf)
+        e = np.exp(s - s.max(axis=1, keepdims=True))
+        out[:, h * d:(h + 1) * d] = (e / e.sum(axis=1, keepdims=True)) @ v
+    return out
+
+
 MUTATIONS = [
     ("linear", _linear_no_bias, [P.test_toy_full_output_matches_printed_values]),
     ("linear", _linear_bias_twice, [P.test_toy_full_output_matches_printed_values,
@@ -108,6 +136,10 @@ MUTATIONS = [
     ("row_shard", _row_shard_wrong_axis, [P.test_toy_row_split_sum_plus_bias_equals_unsharded]),
     ("concat", _concat_reversed, [P.test_toy_column_split_concat_matches_printed_values_and_is_exact]),
     ("qkv_rows", _qkv_rows_shared_kv, [P.test_qkv_head_split_concat_and_one_hot]),
+    ("kv_group_of", _kv_group_round_robin, [P.test_attention_first_causal_row_and_dominant_key]),
+    ("attention_core_shard", _attention_unscaled, [P.test_attention_tiny_by_bruteforce]),
+    ("attention_core_shard", _attention_no_mask, [P.test_attention_uniform_scores_give_prefix_means,
+                                                  P.test_attention_first_causal_row_and_dominant_key]),
     ("kv_heads_of", _kv_heads_of_no_replication, [P.test_kv_heads_replicated_when_more_shards_than_kv_heads]),
 ]
 

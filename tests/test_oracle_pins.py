@@ -236,6 +236,72 @@ def test_kv_heads_replicated_when_more_shards_than_kv_heads():
         np.testing.assert_array_equal(y[:, (hq + 1) * d:], full[:, (nh + nkv + h) * d:(nh + nkv + h + 1) * d])
 
 
+def _qkv(m, hq, hk, d, seed):
+    return I.as_numpy_f64(I.activations(m, (hq + 2 * hk) * d, seed=seed))
+
+
+def test_attention_uniform_scores_give_prefix_means():
+    """K = 0: every allowed key scores the same, so O_i = mean(v_0..v_i) (causal) or the mean of all."""
+    m, hq, hk, d = 6, 2, 1, 4
+    qkv = _qkv(m, hq, hk, d, 61)
+    qkv[:, hq * d:(hq + hk) * d] = 0.0
+    v = qkv[:, (hq + hk) * d:]
+    a = O.attention_core_shard(qkv, hq, hk, d, causal=True)
+    prefix = np.cumsum(v, axis=0) / np.arange(1, m + 1)[:, None]
+    for h in range(hq):
+        np.testing.assert_allclose(a[:, h * d:(h + 1) * d], prefix, rtol=1e-14, atol=1e-15)
+    a2 = O.attention_core_shard(qkv, hq, hk, d, causal=False)
+    np.testing.assert_allclose(a2[:, :d], np.broadcast_to(v.mean(axis=0), (m, d)), rtol=1e-14, atol=1e-15)
+
+
+def test_attention_first_causal_row_and_dominant_key():
+    m, hq, hk, d = 5, 4, 2, 8
+    qkv = _qkv(m, hq, hk, d, 62)
+    a = O.attention_core_shard(qkv, hq, hk, d)
+    for h, g in zip(range(hq), (0, 0, 1, 1)):   # consecutive query heads share a KV head
+        assert O.kv_group_of(h, hq, hk) == g
+        np.testing.assert_array_equal(a[0, h * d:(h + 1) * d], qkv[0, (hq + hk + g) * d:(hq + hk + g + 1) * d])
+    # a key aligned with every query at a huge scale takes all the weight (non-causal)
+    qkv2 = qkv.copy()
+    qkv2[:, :hq * d] = 1.0
+    qkv2[:, hq * d:(hq + hk) * d] = -1.0
+    qkv2[3, hq * d:(hq + hk) * d] = 200.0
+    a2 = O.attention_core_shard(qkv2, hq, hk, d, causal=False)
+    for h, g in zip(range(hq), (0, 0, 1, 1)):
+        np.testing.assert_allclose(a2[:, h * d:(h + 1) * d],
+                                   np.broadcast_to(qkv2[3, (hq + hk + g) * d:(hq + hk + g + 1) * d], (m, d)), rtol=1e-12)
+
+
+def test_attention_tiny_by_bruteforce():
+    m, hq, hk, d = 4, 4, 2, 3
+    qkv = _qkv(m, hq, hk, d, 63)
+    a = O.attention_core_shard(qkv, hq, hk, d)
+    for h in range(hq):
+        g = h // (hq // hk)
+        for i in range(m):
+            sc = [math.fsum(qkv[i, h * d + t] * qkv[j, (hq + g) * d + t] for t in range(d)) / math.sqrt(d)
+                  for j in range(i + 1)]
+            mx = max(sc)
+            w = [math.exp(c - mx) for c in sc]
+            z = math.fsum(w)
+            for t in range(d):
+                o = math.fsum(w[j] * qkv[j, (hq + hk + g) * d + t] for j in range(i + 1)) / z
+                assert abs(a[i, h * d + t] - o) <= 1e-13 * max(1.0, abs(o))
+
+
+def test_attention_shards_equal_unsharded_heads():
+    """Heads are independent: shard r's output is the unsharded attention's block of its heads."""
+    m, nh, nkv, d, p = 7, 8, 2, 4, 2
+    shape = I.LayerShape("t", hidden=16, n_heads=nh, n_kv_heads=nkv, head_dim=d, tp=p, seed=64)
+    wt = {k: I.as_numpy_f64(v) for k, v in I.attn_weights(shape).items()}
+    x = I.as_numpy_f64(I.activations(m, 16, seed=641))
+    full = O.attention_core_shard(O.linear(x, wt["Wqkv"], wt["bqkv"]), nh, nkv, d)
+    for r in range(p):
+        w_r, b_r = O.qkv_shard(wt["Wqkv"], wt["bqkv"], nh, nkv, d, p, r)
+        a_r = O.attention_core_shard(O.col_linear(x, w_r, b_r), nh // p, nkv // p, d)
+        np.testing.assert_allclose(a_r, full[:, r * (nh // p) * d:(r + 1) * (nh // p) * d], rtol=1e-12, atol=1e-14)
+
+
 def test_indivisible_sizes_are_rejected():
     w = np.zeros((10, 9))
     with pytest.raises(ValueError):
