@@ -140,6 +140,21 @@ tp_status_t tp_attn_proj_shard(const void* X, const void* Wqkv_r, const void* bq
                                int32_t head_dim, int32_t tp_size, tp_dtype_t dtype,
                                tp_dtype_t partial_dtype, void* stream);
 
+/* Head-local attention core of shard r, between its QKV projection and its O partial
+ * (heads go to different GPUs, so no exchange: [P4] "How a layer is split"). The core is
+ * not on the pages; this is scaled dot-product attention over the M tokens of one
+ * sequence, grouped-query, causal when `causal` != 0:
+ *   A_r[:, h*d:(h+1)*d] = softmax(Q_h K_g^T / sqrt(d) (+ mask)) V_g,  g = h / (hq/hk)
+ * with Q_h, K_g, V_g the column blocks of QKV_r [M, (hq + 2hk)*d] (segments Q | K | V as
+ * tp_attn_proj_shard writes them; hq = n_heads/p, hk = KV heads per shard, replicated as
+ * for tp_shard_qkv). A_r : [M, hq*d], the input tp_attn_proj_shard's O half expects.
+ * bf16 only (TP_ERR_DTYPE otherwise); head_dim 64 or 128 (TP_ERR_SHAPE otherwise);
+ * TP_ERR_INDIVISIBLE if the heads do not split or group evenly. fp32 softmax and
+ * accumulation, one rounding. */
+tp_status_t tp_attn_core_shard(const void* QKV_r, void* A_r, int64_t M, int32_t n_heads,
+                               int32_t n_kv_heads, int32_t head_dim, int32_t tp_size,
+                               int32_t causal, tp_dtype_t dtype, void* stream);
+
 /* Concat of column-parallel outputs, on one device ([P5] torch.cat([...], dim=-1) and its
  * walkthrough). shards (host array of tp_size device pointers) each hold [M, S] with
  * S = sum(seg_widths) (host array of nseg widths). Segment j of shard r goes to output

@@ -18,7 +18,7 @@ __all__ = [
     "TP_DTYPE_F32", "TP_DTYPE_BF16", "TPError", "lib", "lib_path", "tp_linear_col",
     "tp_linear_row_partial", "tp_mlp_shard", "tp_ffn_gelu_shard", "tp_attn_proj_shard", "tp_combine_concat",
     "tp_combine_sum", "tp_shard_weight", "tp_shard_qkv", "tp_shard_weight_block", "tp_combine_concat_v",
-    "kv_heads_per_shard", "tp_release_workspaces",
+    "kv_heads_per_shard", "tp_attn_core_shard", "tp_release_workspaces",
     "tp_status_string", "EXPORTS",
 ]
 
@@ -42,6 +42,7 @@ _SIGS = {
     "tp_shard_weight": [_vp, _i64, _i64, _i32, _i32, _i32, _vp, _i32, _vp],
     "tp_shard_qkv": [_vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp, _i32, _vp],
     "tp_shard_weight_block": [_vp, _i64, _i64, _i32, _i64, _i64, _vp, _i32, _vp],
+    "tp_attn_core_shard": [_vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _i32, _vp],
     "tp_combine_concat_v": [ctypes.POINTER(_vp), _i32, ctypes.POINTER(_i64), _vp, _i64, _i32, _vp],
     "tp_release_workspaces": [],
     "tp_status_string": [_i32],
@@ -251,6 +252,17 @@ def tp_shard_qkv(Wqkv, in_features: int, n_heads: int, n_kv_heads: int, head_dim
     _call("tp_shard_qkv", _dev(Wqkv, "Wqkv", rows * in_features), in_features, n_heads, n_kv_heads,
           head_dim, tp_size, rank, _dev(Wqkv_r, "Wqkv_r", shard_rows * in_features if shard_rows else None),
           _dt(Wqkv), _stream())
+
+
+def tp_attn_core_shard(QKV_r, A_r, M: int, n_heads: int, n_kv_heads: int, head_dim: int, tp_size: int,
+                       causal: bool = True) -> None:
+    """A_r = head-local (grouped-query, optionally causal) attention over QKV_r's Q | K | V."""
+    hq, hk = _div(n_heads, tp_size), kv_heads_per_shard(n_kv_heads, tp_size)
+    need = hq is not None and hk is not None and M > 0
+    nqkv = (hq + 2 * hk) * head_dim if need else 0
+    _call("tp_attn_core_shard", _dev(QKV_r, "QKV_r", M * nqkv if need else None),
+          _dev(A_r, "A_r", M * hq * head_dim if need else None), M, n_heads, n_kv_heads, head_dim, tp_size,
+          1 if causal else 0, _dt(QKV_r), _stream())
 
 
 def tp_shard_weight_block(W, out_features: int, in_features: int, axis: int, start: int, width: int,

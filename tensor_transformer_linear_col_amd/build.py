@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtp.so")
 ARCH = "gfx950"
 
-SOURCES = ["tp_api.cpp", "k_skinny.hip", "k_gemm.hip", "k_f32.hip", "k_combine.hip"]
+SOURCES = ["tp_api.cpp", "k_skinny.hip", "k_gemm.hip", "k_f32.hip", "k_combine.hip", "k_attn.hip"]
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 anywhere in the device code.
 HIPCC_FLAGS = [

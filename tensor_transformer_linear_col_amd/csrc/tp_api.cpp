@@ -233,6 +233,24 @@ tp_status_t tp_attn_proj_shard(const void* X, const void* Wqkv_r, const void* bq
     return TP_OK;
 }
 
+tp_status_t tp_attn_core_shard(const void* QKV_r, void* A_r, int64_t M, int32_t n_heads, int32_t n_kv_heads,
+                               int32_t head_dim, int32_t tp_size, int32_t causal, tp_dtype_t dtype, void* stream) {
+    if (!QKV_r || !A_r) return TP_ERR_NULL;
+    if (dtype != TP_DTYPE_BF16) return TP_ERR_DTYPE;
+    TP_TRY(check_dims(M, {n_heads, n_kv_heads}));
+    if (tp_size < 1 || tp_size > kMaxTP) return TP_ERR_SHAPE;
+    if (head_dim != 64 && head_dim != 128) return TP_ERR_SHAPE;
+    if (n_heads % tp_size != 0 || kv_heads_per_shard(n_kv_heads, tp_size) == 0) return TP_ERR_INDIVISIBLE;
+    const int64_t hq = n_heads / tp_size, hk = kv_heads_per_shard(n_kv_heads, tp_size);
+    if (hq % hk != 0) return TP_ERR_INDIVISIBLE;  // query heads grouped evenly over the KV heads
+    const int64_t ldq = (hq + 2 * hk) * head_dim, lda = hq * head_dim;
+    TP_TRY(check_vec_operand(QKV_r, ldq, dtype));
+    TP_TRY(check_vec_operand(A_r, lda, dtype));
+    if (M == 0) return TP_OK;
+    return launch_attn_core(QKV_r, ldq, A_r, lda, M, (int)hq, (int)hk, head_dim, causal != 0,
+                            static_cast<hipStream_t>(stream));
+}
+
 tp_status_t tp_combine_concat(const void* const* shards, int32_t tp_size, const int64_t* seg_widths, int32_t nseg,
                               void* Y, int64_t M, tp_dtype_t dtype, void* stream) {
     if (!shards || !seg_widths || !Y) return TP_ERR_NULL;

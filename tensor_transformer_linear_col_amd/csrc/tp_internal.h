@@ -46,6 +46,9 @@ tp_status_t get_workspace(hipStream_t stream, size_t partial_floats, size_t n_co
 tp_status_t launch_skinny(const LinearDesc& d, hipStream_t stream);
 tp_status_t launch_gemm(const LinearDesc& d, hipStream_t stream);
 tp_status_t launch_f32(const LinearDesc& d, hipStream_t stream);
+// Head-local attention core: out[M, hq*d] (row stride lda) from qkv[M, (hq+2hk)*d] (row stride ldq).
+tp_status_t launch_attn_core(const void* qkv, int64_t ldq, void* out, int64_t lda, int64_t M, int hq, int hk, int d,
+                             bool causal, hipStream_t stream);
 
 tp_status_t launch_combine_sum(const void* const* partials, int p, tp_dtype_t pdt, const void* b,
                                void* Y, int64_t M, int64_t N, tp_dtype_t odt, hipStream_t stream);

@@ -31,7 +31,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     for name in names:
         assert hasattr(L, name), name
     assert set(names) == set(tp.EXPORTS)
@@ -136,6 +136,20 @@ def test_uneven_split_entry_points_errors(L):
     bad = (ctypes.c_int64 * 2)(5, 0)
     assert L.tp_combine_concat_v(ptrs, 2, bad, P, 1, F32, None) == SHAPE
     assert L.tp_combine_concat_v(ptrs, 2, ws, 0, 1, F32, None) == NULL
+
+
+def test_attn_core_shard_errors(L):
+    core = lambda **k: L.tp_attn_core_shard(k.get("Q", P), k.get("A", P), k.get("M", 16), k.get("nh", 64),
+                                            k.get("nkv", 8), k.get("d", 128), k.get("p", 8), 1, k.get("dt", BF16), None)
+    assert core(Q=0) == NULL
+    assert core(dt=F32) == DTYPE                     # bf16 only
+    assert core(d=96) == SHAPE
+    assert core(p=3) == INDIV
+    assert core(nh=48, nkv=8, p=12) == INDIV
+    assert core(nh=24, nkv=16, p=8) == INDIV         # 3 query heads cannot group over 2 KV heads
+    assert core(Q=P + 8) == ALIGN
+    assert core(M=0) == OK
+    assert core(M=0, nkv=8, p=16) == OK              # KV heads replicated
 
 
 def test_attn_proj_shard_errors(L):

@@ -1,0 +1,87 @@
+"""GPU parity of the head-local attention core (causal, grouped-query) against the fp64
+oracle, through the C ABI: ragged token counts, both head sizes, the 70B shard's shape, and
+the real chain QKV projection -> attention core -> O partial."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import tensor_transformer_linear_col_amd as tp
+import tp_inputs as I
+from gpu_util import BF16_TOL, canaries_intact, canary_buffer, dev, err, host64, log_case
+
+pytestmark = pytest.mark.gpu
+
+
+def _core(qkv, M, hq, hk, d, causal):
+    buf, A = canary_buffer((M, hq * d), torch.bfloat16)
+    # tp_size = 1: the shard's own head counts
+    tp.tp_attn_core_shard(dev(qkv), A, M, hq, hk, d, 1, causal)
+    torch.cuda.synchronize()
+    return buf, A
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("M", [1, 5, 32, 100, 128, 129, 300])
+def test_attention_core_matches_oracle(M, causal):
+    hq, hk, d = 4, 2, 128
+    log_case("attention core", M, hq, hk, d, causal)
+    qkv = I.activations(M, (hq + 2 * hk) * d, 600 + M)
+    buf, A = _core(qkv, M, hq, hk, d, causal)
+    assert err(A, O.attention_core_shard(host64(qkv), hq, hk, d, causal)) <= BF16_TOL
+    assert canaries_intact(buf, (M, hq * d))
+
+
+@pytest.mark.parametrize("M", [7, 200])
+def test_attention_core_head_dim_64_one_kv_head(M):
+    hq, hk, d = 8, 1, 64
+    log_case("attention core d64", M, hq, hk, d)
+    qkv = I.activations(M, (hq + 2 * hk) * d, 610 + M)
+    buf, A = _core(qkv, M, hq, hk, d, True)
+    assert err(A, O.attention_core_shard(host64(qkv), hq, hk, d, True)) <= BF16_TOL
+    assert canaries_intact(buf, (M, hq * d))
+
+
+def test_attention_core_70b_shard_shape_and_determinism():
+    """8 query heads and 1 KV head of 128 (70B at TP = 8), 2048 tokens."""
+    M, hq, hk, d = 2048, 8, 1, 128
+    log_case("attention core 70b shard", M, hq, hk, d)
+    qkv = I.activations(M, (hq + 2 * hk) * d, 620)
+    _, A1 = _core(qkv, M, hq, hk, d, True)
+    _, A2 = _core(qkv, M, hq, hk, d, True)
+    assert torch.equal(A1, A2)
+    assert err(A1, O.attention_core_shard(host64(qkv), hq, hk, d, True)) <= BF16_TOL
+
+
+def test_attention_chain_qkv_core_o():
+    """X -> QKV_r (column) -> attention core -> P_r (row) on every shard, summed + bo, against
+    the unsharded chain with the real core."""
+    nh, nkv, d, hid, p, M = 8, 2, 128, 512, 2, 96
+    log_case("attention chain", M, nh, nkv, d, hid, p)
+    shape = I.LayerShape("t", hidden=hid, n_heads=nh, n_kv_heads=nkv, head_dim=d, tp=p, seed=63)
+    wt = I.attn_weights(shape)
+    w64 = {k: host64(v) for k, v in wt.items()}
+    x = I.activations(M, hid, 630)
+    X = dev(x)
+    hq, hk = nh // p, nkv // p
+    parts = []
+    for r in range(p):
+        W_r = torch.empty((hq + 2 * hk) * d, hid, dtype=torch.bfloat16, device="cuda")
+        b_r = torch.empty((hq + 2 * hk) * d, dtype=torch.bfloat16, device="cuda")
+        tp.tp_shard_qkv(dev(wt["Wqkv"]), hid, nh, nkv, d, p, r, W_r)
+        tp.tp_shard_qkv(dev(wt["bqkv"]), 1, nh, nkv, d, p, r, b_r)
+        Wo_r = torch.empty(hid, hq * d, dtype=torch.bfloat16, device="cuda")
+        tp.tp_shard_weight(dev(wt["Wo"]), hid, nh * d, p, r, 1, Wo_r)
+        QKV_r = torch.empty(M, (hq + 2 * hk) * d, dtype=torch.bfloat16, device="cuda")
+        A_r = torch.empty(M, hq * d, dtype=torch.bfloat16, device="cuda")
+        P_r = torch.empty(M, hid, dtype=torch.bfloat16, device="cuda")
+        tp.tp_attn_proj_shard(X, W_r, b_r, QKV_r, None, None, None, M, hid, nh, nkv, d, p)
+        tp.tp_attn_core_shard(QKV_r, A_r, M, nh, nkv, d, p, True)
+        tp.tp_attn_proj_shard(None, None, None, None, A_r, Wo_r, P_r, M, hid, nh, nkv, d, p)
+        parts.append(P_r)
+    Y = torch.empty(M, hid, dtype=torch.bfloat16, device="cuda")
+    tp.tp_combine_sum(parts, dev(wt["bo"]), Y, M, hid)
+    torch.cuda.synchronize()
+    qkv = O.linear(host64(x), w64["Wqkv"], w64["bqkv"])
+    a = O.attention_core_shard(qkv, nh, nkv, d, True)
+    assert err(Y, O.linear(a, w64["Wo"], w64["bo"])) <= BF16_TOL
