@@ -148,6 +148,33 @@ class Layer:
         timed("concat", lambda: tp.tp_combine_concat([sh["H"] for sh in self.shards], [self.i], self.Hc, M))
 
 
+def attention_bench(layer, reps=5):
+    """The head-local attention core on each of the layer's 8 shards (its own QKV_r from the
+    timed step: 8 query heads and 1 KV head of 128, causal over the 4096 tokens). Not part of
+    the layer step above, whose attention stand-in is A := Q. Work per shard: 2 products of
+    2 * d flops per (query, allowed key) pair and head: 4 * d * hq * M(M+1)/2."""
+    import torch
+    tp = layer.tp
+    M, p, d = layer.M, layer.p, layer.d
+    hq = layer.nh // p
+    A = torch.empty(M, hq * d, dtype=torch.bfloat16, device="cuda")
+    run = lambda: [tp.tp_attn_core_shard(sh["QKV"], A, M, layer.nh, layer.nkv, d, p, True) for sh in layer.shards]
+    run()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        run()
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / (reps * p)
+    flops = 4.0 * d * hq * M * (M + 1) / 2
+    tf = flops / (us * 1e-6) / 1e12
+    log(f"attention core: {us:.1f} us per shard, {tf:.1f} TFLOP/s")
+    return {"kernel": "attn_kernel (causal GQA, 8 query heads / 1 KV head of 128, 4096 tokens)",
+            "us_per_shard": round(us, 1), "TFLOP_s": round(tf, 1), "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
+
+
 def kernel_ms(ev):
     out = {}
     for name, pairs in ev.items():
@@ -439,6 +466,7 @@ def main():
                               "GB_s": round(sum_bytes / (per["sum"] * 1e-3) / 1e9, 1)}
     kernels["combine_concat"] = {"us_per_launch": round(per["concat"] * 1e3, 1)}
 
+    attention = attention_bench(layer)
     decode = None if args.skip_decode else decode_bench()
     cpu = None if args.skip_cpu_baseline else cpu_baseline(shape, args.cpu_seconds)
 
@@ -460,10 +488,11 @@ def main():
                    "tp_size": layer.p, "tokens": layer.M, "hidden": layer.h, "intermediate": layer.inter,
                    "n_heads": layer.nh, "n_kv_heads": layer.nkv, "head_dim": layer.d,
                    "flop_per_step": layer.total_flops},
-        "roofline": {"kernel": "gemm_kernel gate/up + SwiGLU (one shard, 4096 x 3584 x 8192, x2)",
+        "roofline": {"kernel": "gemm_dtl_kernel gate/up + SwiGLU (one shard, 4096 x 3584 x 8192, x2)",
                      "bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": traffic},
         "kernels": kernels,
+        "attention_core": attention,
         "decode": decode,
         "cpu_baseline": cpu,
     }

@@ -1,6 +1,8 @@
 """GPU parity of the head-local attention core (causal, grouped-query) against the fp64
 oracle, through the C ABI: ragged token counts, both head sizes, the 70B shard's shape, and
-the real chain QKV projection -> attention core -> O partial."""
+the real chain QKV projection -> attention core -> O partial. From 4 query blocks of 128 on
+(M >= 385) the causal core cuts its longer blocks in two key ranges merged through the work
+space (513, 700, 1000, 2048 tokens cover that path, the repeated 2048 call its counters)."""
 import numpy as np
 import pytest
 import torch
@@ -22,7 +24,7 @@ def _core(qkv, M, hq, hk, d, causal):
 
 
 @pytest.mark.parametrize("causal", [True, False])
-@pytest.mark.parametrize("M", [1, 5, 32, 100, 128, 129, 300])
+@pytest.mark.parametrize("M", [1, 5, 32, 100, 128, 129, 300, 513, 1000])
 def test_attention_core_matches_oracle(M, causal):
     hq, hk, d = 4, 2, 128
     log_case("attention core", M, hq, hk, d, causal)
@@ -32,7 +34,7 @@ def test_attention_core_matches_oracle(M, causal):
     assert canaries_intact(buf, (M, hq * d))
 
 
-@pytest.mark.parametrize("M", [7, 200])
+@pytest.mark.parametrize("M", [7, 200, 700])
 def test_attention_core_head_dim_64_one_kv_head(M):
     hq, hk, d = 8, 1, 64
     log_case("attention core d64", M, hq, hk, d)
