@@ -104,6 +104,7 @@ class Layer:
         self.Y1 = torch.empty(M, h, dtype=BF, device="cuda")
         self.Y = torch.empty(M, h, dtype=BF, device="cuda")
         self.QKVc = torch.empty(M, (self.nh + 2 * self.nkv) * self.d, dtype=BF, device="cuda")
+        self.A = torch.empty(M, self.nh * self.d // self.p, dtype=BF, device="cuda")  # one shard's attention output
         self.Hc = torch.empty(M, inter, dtype=BF, device="cuda")
         self.seg = [self.nh // p * self.d, self.nkv // p * self.d, self.nkv // p * self.d]
         # algorithmic work per step (2 M N K per product)
@@ -115,8 +116,9 @@ class Layer:
         }
         self.total_flops = sum(self.flops.values())
 
-    def step(self, ev=None):
-        """One pass of the shard path. ev: optional dict name -> list of (start, end) events."""
+    def step(self, ev=None, core=False):
+        """One pass of the shard path. ev: optional dict name -> list of (start, end) events.
+        core: run the head-local attention core between QKV and O instead of A := Q."""
         tp, torch = self.tp, self.torch
         M, h, p = self.M, self.h, self.p
 
@@ -134,6 +136,11 @@ class Layer:
         for sh in self.shards:
             timed("qkv", lambda: tp.tp_attn_proj_shard(self.X, sh["Wqkv"], sh["bqkv"], sh["QKV"], None, None, None,
                                                       M, h, self.nh, self.nkv, self.d, p))
+            if core:
+                timed("core", lambda: tp.tp_attn_core_shard(sh["QKV"], self.A, M, self.nh, self.nkv, self.d, p, True))
+                timed("o", lambda: tp.tp_linear_row_partial(self.A, self.nh * self.d // p, sh["Wo"], sh["Po"], M,
+                                                            self.nh * self.d, h, p))
+                continue
             # A := Q: the shard's Q heads are the first ka columns of QKV_r (row stride nq)
             timed("o", lambda: tp.tp_linear_row_partial(sh["QKV"], self.nq, sh["Wo"], sh["Po"], M,
                                                         self.nh * self.d, h, p))
@@ -152,7 +159,9 @@ def attention_bench(layer, reps=5):
     """The head-local attention core on each of the layer's 8 shards (its own QKV_r from the
     timed step: 8 query heads and 1 KV head of 128, causal over the 4096 tokens). Not part of
     the layer step above, whose attention stand-in is A := Q. Work per shard: 2 products of
-    2 * d flops per (query, allowed key) pair and head: 4 * d * hq * M(M+1)/2."""
+    2 * d flops per (query, allowed key) pair and head: 4 * d * hq * M(M+1)/2. Also the whole
+    layer step with the core in place of the stand-in (QKV -> core -> O per shard), whose
+    work adds the 8 shards' attention flops to the layer's GEMM flops."""
     import torch
     tp = layer.tp
     M, p, d = layer.M, layer.p, layer.d
@@ -171,8 +180,53 @@ def attention_bench(layer, reps=5):
     flops = 4.0 * d * hq * M * (M + 1) / 2
     tf = flops / (us * 1e-6) / 1e12
     log(f"attention core: {us:.1f} us per shard, {tf:.1f} TFLOP/s")
+
+    layer.step(core=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        layer.step(core=True)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    lflops = layer.total_flops + p * flops
+    ltf = lflops / (ms * 1e-3) / 1e12
+    log(f"layer step with the attention core: {ms:.3f} ms, {ltf:.1f} TFLOP/s")
     return {"kernel": "attn_kernel (causal GQA, 8 query heads / 1 KV head of 128, 4096 tokens)",
-            "us_per_shard": round(us, 1), "TFLOP_s": round(tf, 1), "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
+            "us_per_shard": round(us, 1), "TFLOP_s": round(tf, 1), "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
+            "layer_step_with_core": {"ms_per_step": round(ms, 4), "GFLOP": round(lflops / 1e9, 1),
+                                     "TFLOP_s": round(ltf, 1)}}
+
+
+def attention_decode_bench(reps=50):
+    """One decode step of the attention core over a KV cache on the 70B TP=8 shard (8 query
+    heads, 1 KV head of 128): new tokens M appended at position T, attention over T + M keys.
+    Bytes: the K and V cache rows read once, (T + M) * 2 * 128 * 2."""
+    import torch
+    import tensor_transformer_linear_col_amd as tp
+    nh, nkv, d, p = 64, 8, 128, 8
+    hq, hk = nh // p, nkv // p
+    g = torch.Generator().manual_seed(7)
+    out = []
+    for T in (4096, 32768):
+        Kc = torch.randn(T + 64, hk * d, generator=g).to(torch.bfloat16).cuda()
+        Vc = torch.randn(T + 64, hk * d, generator=g).to(torch.bfloat16).cuda()
+        for M in (1, 16):
+            Q = torch.randn(M, (hq + 2 * hk) * d, generator=g).to(torch.bfloat16).cuda()
+            A = torch.empty(M, hq * d, dtype=torch.bfloat16, device="cuda")
+            tp.tp_attn_decode_shard(Q, Kc, Vc, T, A, M, nh, nkv, d, p)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                tp.tp_attn_decode_shard(Q, Kc, Vc, T, A, M, nh, nkv, d, p)
+            b.record()
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) * 1e3 / reps
+            gbs = (T + M) * 2 * hk * d * 2 / (us * 1e-6) / 1e9
+            log(f"attention decode T={T} M={M}: {us:.1f} us, {gbs:.0f} GB/s")
+            out.append({"cache_len": T, "M": M, "us": round(us, 2), "GB_s": round(gbs, 1)})
+    return {"kernels": "copy2d_kernel x2 (append K, V) + attn_kernel (packed query heads, cut keys)", "steps": out}
 
 
 def kernel_ms(ev):
@@ -468,6 +522,7 @@ def main():
 
     attention = attention_bench(layer)
     decode = None if args.skip_decode else decode_bench()
+    attention_decode = None if args.skip_decode else attention_decode_bench()
     cpu = None if args.skip_cpu_baseline else cpu_baseline(shape, args.cpu_seconds)
 
     out = {
@@ -494,6 +549,7 @@ def main():
         "kernels": kernels,
         "attention_core": attention,
         "decode": decode,
+        "attention_decode": attention_decode,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -155,6 +155,24 @@ tp_status_t tp_attn_core_shard(const void* QKV_r, void* A_r, int64_t M, int32_t 
                                int32_t n_kv_heads, int32_t head_dim, int32_t tp_size,
                                int32_t causal, tp_dtype_t dtype, void* stream);
 
+/* One decode step of the head-local attention core over shard r's KV cache (each GPU keeps
+ * the keys and values of its own KV heads: [P4] "How a layer is split"; "Why it helps when
+ * serving" on the memory that splitting frees for the cache). The new tokens' projections
+ * QKV_r [M, (hq + 2hk)*d] (as tp_attn_proj_shard writes them) sit at positions
+ * cache_len .. cache_len + M - 1. The call first appends their K and V rows to the caches
+ *   K_cache_r, V_cache_r : [capacity, hk*d] token-major (row t = the shard's KV heads at
+ *   position t; caller-owned, rows 0 .. cache_len - 1 already filled),
+ * then computes, with n = cache_len + M keys and the core's definition (tp_attn_core_shard),
+ *   A_r[i, h*d:(h+1)*d] = softmax(Q_h[i] K_g[0 .. cache_len + i]^T / sqrt(d)) V_g[0 .. cache_len + i]
+ * i.e. every new token sees the whole cache and the new tokens up to itself. A_r : [M, hq*d].
+ * The caller advances cache_len by M afterwards. TP_ERR_SHAPE if cache_len + M > capacity or
+ * a K/V cache exceeds 2 GiB; bf16 only; head_dim 64 or 128; the head rules of
+ * tp_attn_core_shard. */
+tp_status_t tp_attn_decode_shard(const void* QKV_r, void* K_cache_r, void* V_cache_r, int64_t cache_len,
+                                 int64_t capacity, void* A_r, int64_t M, int32_t n_heads,
+                                 int32_t n_kv_heads, int32_t head_dim, int32_t tp_size,
+                                 tp_dtype_t dtype, void* stream);
+
 /* Concat of column-parallel outputs, on one device ([P5] torch.cat([...], dim=-1) and its
  * walkthrough). shards (host array of tp_size device pointers) each hold [M, S] with
  * S = sum(seg_widths) (host array of nseg widths). Segment j of shard r goes to output

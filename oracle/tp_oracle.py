@@ -389,6 +389,30 @@ def attention_core_shard(qkv_r, hq, hk, d, causal=True):
     return out
 
 
+def attention_decode_shard(qkv_new, k_cache, v_cache, hq, hk, d):
+    """Decode step over a KV cache: the new tokens' projections qkv_new[M, (hq + 2 hk) d] sit at
+    positions T .. T + M - 1 after the T cached rows k_cache, v_cache [T, hk d] (KV head g at
+    columns g*d). Token i sees keys 0 .. T + i: the cache and the new tokens up to itself.
+    Returns (A[M, hq*d], the caches with the new rows appended)."""
+    qkv_new, k_cache, v_cache = f64(qkv_new), f64(k_cache), f64(v_cache)
+    m, t = qkv_new.shape[0], k_cache.shape[0]
+    k_all = np.concatenate([k_cache, qkv_new[:, hq * d:(hq + hk) * d]], axis=0)
+    v_all = np.concatenate([v_cache, qkv_new[:, (hq + hk) * d:(hq + 2 * hk) * d]], axis=0)
+    out = np.empty((m, hq * d))
+    for h in range(hq):
+        g = kv_group_of(h, hq, hk)
+        q = qkv_new[:, h * d:(h + 1) * d]
+        k = k_all[:, g * d:(g + 1) * d]
+        v = v_all[:, g * d:(g + 1) * d]
+        s = (q @ k.T) / math.sqrt(d)
+        allowed = np.arange(t + m)[None, :] <= (t + np.arange(m))[:, None]
+        s = np.where(allowed, s, -np.inf)
+        s = s - s.max(axis=1, keepdims=True)
+        e = np.exp(s)
+        out[:, h * d:(h + 1) * d] = (e / e.sum(axis=1, keepdims=True)) @ v
+    return out, k_all, v_all
+
+
 # ---------------------------------------------------------------------------
 # Full layer chain with the attention-core stand-in A := Q (a reading: the core
 # is not on the pages).  X -> QKV -> A := Q -> Y1 = sum_r O-partials + bo

@@ -18,7 +18,7 @@ __all__ = [
     "TP_DTYPE_F32", "TP_DTYPE_BF16", "TPError", "lib", "lib_path", "tp_linear_col",
     "tp_linear_row_partial", "tp_mlp_shard", "tp_ffn_gelu_shard", "tp_attn_proj_shard", "tp_combine_concat",
     "tp_combine_sum", "tp_shard_weight", "tp_shard_qkv", "tp_shard_weight_block", "tp_combine_concat_v",
-    "kv_heads_per_shard", "tp_attn_core_shard", "tp_release_workspaces",
+    "kv_heads_per_shard", "tp_attn_core_shard", "tp_attn_decode_shard", "tp_release_workspaces",
     "tp_status_string", "EXPORTS",
 ]
 
@@ -43,6 +43,7 @@ _SIGS = {
     "tp_shard_qkv": [_vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp, _i32, _vp],
     "tp_shard_weight_block": [_vp, _i64, _i64, _i32, _i64, _i64, _vp, _i32, _vp],
     "tp_attn_core_shard": [_vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _i32, _vp],
+    "tp_attn_decode_shard": [_vp, _vp, _vp, _i64, _i64, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp],
     "tp_combine_concat_v": [ctypes.POINTER(_vp), _i32, ctypes.POINTER(_i64), _vp, _i64, _i32, _vp],
     "tp_release_workspaces": [],
     "tp_status_string": [_i32],
@@ -263,6 +264,23 @@ def tp_attn_core_shard(QKV_r, A_r, M: int, n_heads: int, n_kv_heads: int, head_d
     _call("tp_attn_core_shard", _dev(QKV_r, "QKV_r", M * nqkv if need else None),
           _dev(A_r, "A_r", M * hq * head_dim if need else None), M, n_heads, n_kv_heads, head_dim, tp_size,
           1 if causal else 0, _dt(QKV_r), _stream())
+
+
+def tp_attn_decode_shard(QKV_r, K_cache_r, V_cache_r, cache_len: int, A_r, M: int, n_heads: int,
+                         n_kv_heads: int, head_dim: int, tp_size: int) -> None:
+    """Append the M new tokens' K/V rows of QKV_r to the shard's caches at cache_len, then
+    A_r = causal attention of the new tokens over the cache and themselves. The caches are
+    [capacity, hk*head_dim] tensors; the capacity is read from K_cache_r's size."""
+    hq, hk = _div(n_heads, tp_size), kv_heads_per_shard(n_kv_heads, tp_size)
+    need = hq is not None and hk is not None
+    nqkv = (hq + 2 * hk) * head_dim if need else 0
+    ldkv = hk * head_dim if need else 0
+    capacity = K_cache_r.numel() // ldkv if need and ldkv > 0 else 0
+    _call("tp_attn_decode_shard", _dev(QKV_r, "QKV_r", M * nqkv if need else None),
+          _dev(K_cache_r, "K_cache_r", capacity * ldkv if need else None),
+          _dev(V_cache_r, "V_cache_r", capacity * ldkv if need else None), cache_len, capacity,
+          _dev(A_r, "A_r", M * hq * head_dim if need else None), M, n_heads, n_kv_heads, head_dim, tp_size,
+          _dt(QKV_r), _stream())
 
 
 def tp_shard_weight_block(W, out_features: int, in_features: int, axis: int, start: int, width: int,

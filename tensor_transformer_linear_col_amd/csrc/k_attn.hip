@@ -30,6 +30,7 @@
 // The causal mask and the sequence-end mask are applied only on blocks that need them.
 // O^T registers hold one query per lane, so the rescale, the merge and the final 1/l
 // are per-lane scalars. Softmax and accumulation are fp32; A_r is rounded once to bf16.
+#include <algorithm>
 #include <type_traits>
 
 #include "tp_internal.h"
@@ -38,30 +39,43 @@ namespace tp {
 namespace {
 
 struct AttnParams {
-    const bf16* qkv;  // [M, ldq]
-    int64_t ldq;
-    bf16* out;        // [M, lda]
-    int64_t lda;
-    int M, hq, hk;
+    const bf16* q;  // query rows: token i, head h at q + i * ldq + h * d
+    const bf16* k;  // key rows: position t of KV head g at k + t * ldk + g * d
+    const bf16* v;  // value rows: position t of KV head g at v + t * ldv + g * d
+    bf16* out;      // A: token i, head h at out + i * lda + h * d
+    int64_t ldq, ldk, ldv, lda;
+    int M;     // query tokens, at positions pos0 .. pos0 + M - 1
+    int Nk;    // keys (positions 0 .. Nk - 1)
+    int pos0;  // position of query token 0 (Nk - M)
+    int hq, hk;
     float scale_log2;  // log2(e) / sqrt(d)
-    // Causal balance: the units (head, query block) of the query blocks >= qsplit are
-    // cut in two key ranges handled by two workgroups (nsu such units); each leaves its
-    // unnormalised partial in ws, and the second to arrive merges and stores.
-    int qsplit, nsu;
-    float* ws;
-    unsigned* counters;
+    // A workgroup holds 128 query rows of one query block: PACK = false, 128 tokens of one
+    // query head; PACK = true (few tokens, e.g. decode), rows = (token, head) pairs of one
+    // KV group, row r = token r / Gq, head g * Gq + r % Gq (Gq = hq / hk), so the group's
+    // query heads share every K/V block. The keys of a query block (nkb blocks of 64)
+    // are cut in ceil(nkb / L) near-equal ranges, one workgroup each (L = 0: no cut);
+    // each leaves its unnormalised partial in ws, and the last of a query block to
+    // arrive merges them in range order and stores.
+    // With PACK the ranges leave their partials with plain stores and attn_merge_kernel, the
+    // next launch, merges them: O^T rows at ws[slot][row][d], (m, l) at ws[ml_off + (slot *
+    // 128 + row) * 2].
+    int L;
+    float* ws;          // one partial slot per workgroup (indexed like blockIdx)
+    unsigned* counters; // one arrival counter per query block (without PACK)
+    int64_t ml_off;
 };
 
-constexpr int KB = 64;   // keys per block
+constexpr int KB = 64;  // keys per block
 
-// 16 bytes at byte offset voff + soff of a raw buffer descriptor over [base, base + bytes):
-// reads past the end return zeros instead of faulting. The descriptor type exists only for
-// the GPU target, so the body is compiled in the device pass alone.
-__device__ __forceinline__ bf16x8 load16(const void* base, uint32_t bytes, uint32_t voff, uint32_t soff) {
+// 16 bytes at byte offset off of a raw buffer descriptor over [base, base + bytes): a lane
+// whose offset lies past the end reads zeros instead of touching memory (the bound check
+// covers the per-lane offset, so the whole offset is passed there). The descriptor type
+// exists only for the GPU target, so the body is compiled in the device pass alone.
+__device__ __forceinline__ bf16x8 load16(const void* base, uint32_t bytes, uint32_t off) {
 #if defined(__HIP_DEVICE_COMPILE__)
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, soff, 0));
+    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0));
 #else
     return bf16x8{};
 #endif
@@ -73,10 +87,10 @@ __device__ __forceinline__ int vpos(int k) {
     return (k & ~15) | ((((g & 1) << 1) | (g >> 1)) << 2) | (k & 3);
 }
 
-template <int D, bool CAUSAL, int WQ>
+template <int D, bool CAUSAL, bool PACK, int WQ>
 __global__ __launch_bounds__(128 * WQ, 2) void attn_kernel(AttnParams p) {
     static_assert(D == 64 || D == 128, "head_dim 64 or 128");
-    constexpr int QB = 32 * WQ;            // queries per workgroup
+    constexpr int QB = 32 * WQ;            // query rows per workgroup
     constexpr int NT = 128 * WQ;           // threads: WQ query slices x 2 key halves
     constexpr int KP = D * 2 + 16;         // K tile row pitch (bytes): 16-byte pad
     constexpr int VP = KB * 2 + 16;        // V^T tile row pitch (bytes): 16-byte pad
@@ -88,8 +102,9 @@ __global__ __launch_bounds__(128 * WQ, 2) void attn_kernel(AttnParams p) {
     constexpr int R = CK;                  // keys per thread in the V transpose
     constexpr int NKG = KB / R;            // key groups of the V transpose
     static_assert(CK >= 1 && NKG * (D / 8) == NT, "staging covers the tile");
+    constexpr int NR = NB * 16 + 2;        // floats per lane of a partial: O^T, m, l
     // LDS: two block buffers; after the loop the same bytes hold the merge data.
-    constexpr int MERGEB = WQ * 64 * (NB * 16 + 2) * 4;
+    constexpr int MERGEB = WQ * 64 * NR * 4;
     constexpr int LDSB = 2 * STG > MERGEB ? 2 * STG : MERGEB;
     __shared__ __attribute__((aligned(16))) char lds[LDSB];
 
@@ -97,34 +112,52 @@ __global__ __launch_bounds__(128 * WQ, 2) void attn_kernel(AttnParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wq = wave % WQ, kh = wave / WQ;  // query slice, key half
     const int l32 = lane & 31, lh = lane >> 5;
-    const int nqb = (p.M + QB - 1) / QB;
-    // Workgroup -> (head, query block, key range). The halves of the split units come
-    // first, then the whole units, each from the longest (causal) query block down.
-    int h, qblk, part = -1, unit = 0;
-    if ((int)blockIdx.x < 2 * p.nsu) {
-        const int b = blockIdx.x;
-        h = b % p.hq;
-        part = (b / p.hq) % 2;
-        qblk = nqb - 1 - b / (2 * p.hq);
-        unit = (nqb - 1 - qblk) * p.hq + h;
-    } else {
-        const int b = blockIdx.x - 2 * p.nsu;
-        h = b % p.hq;
-        qblk = p.qsplit - 1 - b / p.hq;
+    const int gq = p.hq / p.hk;                       // query heads per KV head
+    const int HM = PACK ? p.hk : p.hq;                // workgroups per query block
+    const int rows = PACK ? p.M * gq : p.M;           // query rows of one workgroup column
+    const int nqb = (rows + QB - 1) / QB;
+    // Last query token of query block b and the keys it needs.
+    auto last_tok = [&](int b) { return PACK ? min(p.M - 1, ((b + 1) * QB - 1) / gq) : min(p.M - 1, (b + 1) * QB - 1); };
+    auto kend_of = [&](int b) { return CAUSAL ? min(p.Nk, p.pos0 + last_tok(b) + 1) : p.Nk; };
+
+    // Workgroup -> (head or KV group, query block, key range): blockIdx = piece * HM + hm,
+    // pieces enumerated from the last (longest, when causal) query block down and, within
+    // one, in key order. base = the first piece of this query block.
+    const int hm = blockIdx.x % HM;
+    int qblk, np = 1, part = 0, base = 0;
+    {
+        int b = blockIdx.x / HM;
+        if (p.L > 0) {
+            // A scalar walk over the query blocks; its length grows like L, i.e. like the
+            // work of every piece, so its share stays small.
+            for (qblk = nqb - 1;; --qblk) {
+                np = ((kend_of(qblk) - 1) / KB + p.L) / p.L;  // ceil(nkb / L)
+                if (b < np) break;
+                b -= np;
+                base += np;
+            }
+            part = b;
+        } else {
+            qblk = nqb - 1 - b;
+        }
     }
-    const int g = h / (p.hq / p.hk);
-    const int q0 = qblk * QB, qw = q0 + wq * 32;
-    const int qi = qw + l32;  // this lane's query
-    const bf16* Q = p.qkv + (int64_t)h * D;
-    const bf16* K = p.qkv + (int64_t)(p.hq + g) * D;
-    const bf16* V = p.qkv + (int64_t)(p.hq + p.hk + g) * D;
+    const int g = PACK ? hm : hm / gq;  // KV head
+    const int row = qblk * QB + wq * 32 + l32;         // this lane's query row
+    const int qi = PACK ? row / gq : row;              // its token
+    const int h = PACK ? g * gq + row % gq : hm;       // its query head
+    const int qpos = p.pos0 + qi;                      // its position
+    // This wave's last token (rows past the end count as the last token).
+    const int wlast = PACK ? min(p.M - 1, (qblk * QB + wq * 32 + 31) / gq) : min(p.M - 1, qblk * QB + wq * 32 + 31);
+    const int wfirst = PACK ? (qblk * QB + wq * 32) / gq : qblk * QB + wq * 32;
+    const bf16* K = p.k + (int64_t)g * D;
+    const bf16* V = p.v + (int64_t)g * D;
     const float c = p.scale_log2;
     const float thr = 8.f / c;  // raw-score margin before m is raised
 
     // The wave's queries as the B operand of S^T: chunk j holds d 16j + 8lh .. +7.
     bf16x8 qf[NC];
     {
-        const bf16* qrow = Q + (int64_t)min(qi, p.M - 1) * p.ldq + 8 * lh;
+        const bf16* qrow = p.q + (int64_t)min(qi, p.M - 1) * p.ldq + (int64_t)h * D + 8 * lh;
 #pragma unroll
         for (int j = 0; j < NC; ++j) qf[j] = *reinterpret_cast<const bf16x8*>(qrow + 16 * j);
         // Consume the loads here: otherwise the wait for them lands inside the key loop,
@@ -140,36 +173,37 @@ __global__ __launch_bounds__(128 * WQ, 2) void attn_kernel(AttnParams p) {
         for (int e = 0; e < 16; ++e) acc[b][e] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
-    // Key blocks: all keys of the sequence, or (causal) those up to the block's last query.
-    const int kend = CAUSAL ? min(p.M, q0 + QB) : p.M;
-    const int nkb_all = (kend + KB - 1) / KB;
-    const int kb0 = part == 1 ? nkb_all / 2 : 0;
-    const int nkb = part == 0 ? nkb_all / 2 : nkb_all;  // this workgroup's blocks: [kb0, nkb)
-    const int wave_kend = CAUSAL ? min(p.M, qw + 32) : p.M;  // this wave needs keys < wave_kend
+    // Key blocks: all keys, or (causal) those up to the block's last query.
+    const int nkb_all = (kend_of(qblk) + KB - 1) / KB;
+    const int kb0 = part * nkb_all / np;
+    const int nkb = (part + 1) * nkb_all / np;  // this workgroup's blocks: [kb0, nkb)
+    // This wave needs keys < wave_kend; a wave whose rows all lie past the last token needs none.
+    const int wave_kend = wfirst >= p.M ? 0 : CAUSAL ? min(p.Nk, p.pos0 + wlast + 1) : p.Nk;
 
     // Global -> registers through buffer loads whose bound is the end of the last key (or
-    // value) row, so keys past M read as zeros (they are masked below) and the per-thread
-    // offsets are fixed: only the block's scalar row offset changes.
+    // value) row, so keys past Nk read as zeros (they are masked below) and never touch
+    // memory past the operand; the per-thread offsets are fixed, plus the block's row offset.
     // K: chunk i of thread t is key (t + NT i) / (D/8), d offset 8 * ((t + NT i) % (D/8))
-    // (rows read whole). V (threads t < NVT): keys 2*kg, 2*kg + 1 (kg = t % NKG) at
+    // (rows read whole). V: thread t holds keys R*kg .. R*kg+R-1 (kg = t % NKG) at
     // d 8*dv .. 8*dv+7 (dv = t / NKG), ready to be written transposed.
     const int kg = tid % NKG, dv = tid / NKG;
-    const uint32_t kv_bytes = (uint32_t)(((int64_t)(p.M - 1) * p.ldq + D) * 2);
+    const uint32_t k_bytes = (uint32_t)(((int64_t)(p.Nk - 1) * p.ldk + D) * 2);
+    const uint32_t v_bytes = (uint32_t)(((int64_t)(p.Nk - 1) * p.ldv + D) * 2);
     uint32_t koff[CK], voff[R];
 #pragma unroll
     for (int i = 0; i < CK; ++i) {
         const int ch = tid + NT * i;
-        koff[i] = (uint32_t)(((ch / (D / 8)) * p.ldq + 8 * (ch % (D / 8))) * 2);
+        koff[i] = (uint32_t)(((ch / (D / 8)) * p.ldk + 8 * (ch % (D / 8))) * 2);
     }
 #pragma unroll
-    for (int j = 0; j < R; ++j) voff[j] = (uint32_t)(((R * kg + j) * p.ldq + 8 * dv) * 2);
+    for (int j = 0; j < R; ++j) voff[j] = (uint32_t)(((R * kg + j) * p.ldv + 8 * dv) * 2);
     bf16x8 kr[CK], vr[R];
     auto fetch = [&](int kb) {
-        const uint32_t soff = (uint32_t)(kb * KB * p.ldq * 2);
+        const uint32_t ko = (uint32_t)(kb * KB * p.ldk * 2), vo = (uint32_t)(kb * KB * p.ldv * 2);
 #pragma unroll
-        for (int i = 0; i < CK; ++i) kr[i] = load16(K, kv_bytes, koff[i], soff);
+        for (int i = 0; i < CK; ++i) kr[i] = load16(K, k_bytes, koff[i] + ko);
 #pragma unroll
-        for (int j = 0; j < R; ++j) vr[j] = load16(V, kv_bytes, voff[j], soff);
+        for (int j = 0; j < R; ++j) vr[j] = load16(V, v_bytes, voff[j] + vo);
     };
     auto stage = [&](char* buf) {
 #pragma unroll
@@ -224,12 +258,13 @@ __global__ __launch_bounds__(128 * WQ, 2) void attn_kernel(AttnParams p) {
                 for (int b = 0; b < NB; ++b)
                     vf[st][b] = *reinterpret_cast<const bf16x8*>(vts + (32 * b + l32) * VP + (32 * kh + 16 * st + 8 * lh) * 2);
 
-            // Masks (keys past M; causal: keys after the query), only where a key can fail them.
-            if (k0 + 32 > p.M || (CAUSAL && k0 + 31 > qw)) {
+            // Masks (keys past Nk; causal: keys after the query's position), only where a key
+            // can fail them.
+            if (k0 + 32 > p.Nk || (CAUSAL && k0 + 31 > p.pos0 + wfirst)) {
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int key = k0 + 8 * (e / 4) + 4 * lh + (e % 4);
-                    const bool ok = key < p.M && (!CAUSAL || key <= qi);
+                    const bool ok = key < p.Nk && (!CAUSAL || key <= qpos);
                     s[e] = ok ? s[e] : -INFINITY;
                 }
             }
@@ -278,7 +313,6 @@ __global__ __launch_bounds__(128 * WQ, 2) void attn_kernel(AttnParams p) {
 
     // Merge the two key halves: wave w + WQ leaves (m, l, O^T) in LDS, wave w combines.
     // Lane order in the merge area: [wave slice][register][lane], conflict-free.
-    constexpr int NR = NB * 16 + 2;  // floats per lane: O^T, m, l
     l_run += __shfl_xor(l_run, 32);
     __syncthreads();  // every wave is done with the block buffers
     float* mg = reinterpret_cast<float*>(lds) + wq * 64 * NR;
@@ -292,11 +326,8 @@ __global__ __launch_bounds__(128 * WQ, 2) void attn_kernel(AttnParams p) {
     }
     __syncthreads();
     // (m, l, O^T) of two partial results over disjoint keys -> one. A part that saw no
-    // valid key has m = -inf and l = 0: weight 0. Symmetric in its two operands (products
-    // rounded separately, no fused multiply-add), so the result does not depend on which is
-    // "this" one, i.e. on which workgroup of a split unit arrives last.
+    // valid key has m = -inf and l = 0: weight 0.
     auto merge = [&](float m2, float l2, auto&& other) {
-#pragma clang fp contract(off)
         const float mm = fmaxf(m_run, m2);
         const float a1 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run - mm) * c);
         const float a2 = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m2 - mm) * c);
@@ -310,35 +341,72 @@ __global__ __launch_bounds__(128 * WQ, 2) void attn_kernel(AttnParams p) {
     if (kh == 0)
         merge(mg[NB * 16 * 64 + lane], mg[(NB * 16 + 1) * 64 + lane], [&](int r) { return mg[r * 64 + lane]; });
 
-    if (part >= 0) {
-        // Split unit: leave this half's partial in its slot, then the second workgroup to
-        // arrive merges the two. The partials move only through device-scope atomic
-        // stores and loads, coherent across the XCDs' L2 caches by themselves; waiting for
-        // the stores before the arrival counter is incremented orders them.
+    if (PACK && np > 1) {
+        // Decode: this range's partial goes out with plain stores; attn_merge_kernel merges
+        // all ranges of the query block at once (a kernel boundary orders the two).
+        if (kh == 0 && wfirst < p.M) {
+            const int64_t sl = (int64_t)(base + part) * HM + hm;
+            const int r = wq * 32 + l32;
+            float* o = p.ws + (sl * QB + r) * D;
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<floatx4*>(o + 32 * b + 8 * q + 4 * lh) =
+                        floatx4{acc[b][4 * q], acc[b][4 * q + 1], acc[b][4 * q + 2], acc[b][4 * q + 3]};
+            if (lh == 0) {
+                p.ws[p.ml_off + (sl * QB + r) * 2] = m_run;
+                p.ws[p.ml_off + (sl * QB + r) * 2 + 1] = l_run;
+            }
+        }
+        return;
+    }
+    if (np > 1) {
+        // Cut query block: leave this range's partial in the workgroup's slot; the last
+        // workgroup of the block to arrive merges all of them in key order (so the result
+        // does not depend on the arrival order). The partials move only through
+        // device-scope atomic stores and loads, coherent across the XCDs' L2 caches by
+        // themselves; waiting for the stores before the arrival counter is incremented
+        // orders them.
         __shared__ unsigned is_last;
-        float* slot = p.ws + ((int64_t)unit * 2 + part) * (WQ * 64 * NR) + wq * 64 * NR;
+        auto slot = [&](int part_) { return p.ws + ((int64_t)(base + part_) * HM + hm) * (WQ * 64 * NR) + wq * 64 * NR; };
+        const int unit = (nqb - 1 - qblk) * HM + hm;
         if (kh == 0) {
+            float* mine = slot(part);
 #pragma unroll
             for (int b = 0; b < NB; ++b)
 #pragma unroll
                 for (int e = 0; e < 16; ++e)
-                    __hip_atomic_store(slot + (b * 16 + e) * 64 + lane, acc[b][e], __ATOMIC_RELAXED,
+                    __hip_atomic_store(mine + (b * 16 + e) * 64 + lane, acc[b][e], __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(slot + NB * 16 * 64 + lane, m_run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(slot + (NB * 16 + 1) * 64 + lane, l_run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(mine + NB * 16 * 64 + lane, m_run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(mine + (NB * 16 + 1) * 64 + lane, l_run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         __builtin_amdgcn_s_waitcnt(0);  // vmcnt = expcnt = lgkmcnt = 0: stores acknowledged
         __syncthreads();
         if (tid == 0) {
             const unsigned prev = __hip_atomic_fetch_add(p.counters + unit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            is_last = prev == 1u ? 1u : 0u;
-            if (prev == 1u) __hip_atomic_store(p.counters + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            is_last = prev == (unsigned)(np - 1) ? 1u : 0u;
+            if (is_last) __hip_atomic_store(p.counters + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         __syncthreads();
         if (!is_last) return;
-        const float* other = p.ws + ((int64_t)unit * 2 + (1 - part)) * (WQ * 64 * NR) + wq * 64 * NR;
-        auto ld = [&](int r) { return __hip_atomic_load(other + r * 64 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
-        if (kh == 0) merge(ld(NB * 16), ld(NB * 16 + 1), ld);
+        if (kh == 0) {
+            auto ld = [&](const float* src, int r) {
+                return __hip_atomic_load(src + r * 64 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            };
+            const float* s0 = slot(0);
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[b][e] = ld(s0, b * 16 + e);
+            m_run = ld(s0, NB * 16);
+            l_run = ld(s0, NB * 16 + 1);
+            for (int q = 1; q < np; ++q) {
+                const float* sq = slot(q);
+                merge(ld(sq, NB * 16), ld(sq, NB * 16 + 1), [&](int r) { return ld(sq, r); });
+            }
+        }
     }
     if (kh == 1 || qi >= p.M) return;
 
@@ -355,49 +423,174 @@ __global__ __launch_bounds__(128 * WQ, 2) void attn_kernel(AttnParams p) {
         }
 }
 
-constexpr int kWQ = 4;  // query slices per workgroup: 128 queries, 8 waves
+constexpr int kWQ = 4;  // query slices per workgroup: 128 query rows, 8 waves
 
-template <int D, bool CAUSAL>
+// Merge of the key ranges of cut packed query blocks: one workgroup per (query block, KV
+// head, row); thread (j, d4) takes the ranges q = j, j + 8, ... (independent loads, all in
+// flight at once) for 4 consecutive d, merging them online in that order; the 8 partial
+// results then meet through LDS in j order. Fixed order throughout, one division by the
+// merged sum, one rounding.
+template <int D>
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p, int nqb) {
+    constexpr int QB = 32 * kWQ, NJ = 256 / (D / 4);  // range lanes: 8 (D = 128) or 16 (D = 64)
+    __shared__ float sm[NJ], sl_[NJ];
+    __shared__ floatx4 so[NJ][D / 4];
+    const int gq = p.hq / p.hk, HM = p.hk;
+    const int d4 = threadIdx.x % (D / 4), j = threadIdx.x / (D / 4);
+    const int row = blockIdx.x % QB;
+    const int u = blockIdx.x / QB;
+    const int hm = u % HM, qblk = nqb - 1 - u / HM;
+    const int grow = qblk * QB + row;
+    const int tok = grow / gq, h = hm * gq + grow % gq;
+    if (tok >= p.M) return;  // uniform per workgroup
+    auto np_of = [&](int b) {
+        const int last = min(p.M - 1, ((b + 1) * QB - 1) / gq);
+        return ((min(p.Nk, p.pos0 + last + 1) - 1) / KB + p.L) / p.L;
+    };
+    int base = 0;
+    for (int b = nqb - 1; b > qblk; --b) base += np_of(b);
+    const int np = np_of(qblk);
+    if (np <= 1) return;  // an uncut query block stored its own result
+    const float c = p.scale_log2;
+    // Merge (m2, l2, o2) into (m, l, o); a part that saw no valid key (m = -inf, l = 0) has weight 0.
+    auto merge = [&](float& m, float& l, floatx4& o, float m2, float l2, const floatx4& o2) {
+        const float mn = fmaxf(m, m2);
+        const float a = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - mn) * c);
+        const float w = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m2 - mn) * c);
+        l = l * a + l2 * w;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) o[t] = o[t] * a + o2[t] * w;
+        m = mn;
+    };
+    float m = -INFINITY, l = 0.f;
+    floatx4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int q = j; q < np; q += NJ) {
+        const int64_t sl = (int64_t)(base + q) * HM + hm;
+        merge(m, l, o, p.ws[p.ml_off + (sl * QB + row) * 2], p.ws[p.ml_off + (sl * QB + row) * 2 + 1],
+              *reinterpret_cast<const floatx4*>(p.ws + (sl * QB + row) * D + 4 * d4));
+    }
+    if (d4 == 0) {
+        sm[j] = m;
+        sl_[j] = l;
+    }
+    so[j][d4] = o;
+    __syncthreads();
+    if (j != 0) return;
+    for (int jj = 1; jj < NJ; ++jj) merge(m, l, o, sm[jj], sl_[jj], so[jj][d4]);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const bf16x4 v = {(bf16)(o[0] * inv), (bf16)(o[1] * inv), (bf16)(o[2] * inv), (bf16)(o[3] * inv)};
+    *reinterpret_cast<bf16x4*>(p.out + (int64_t)tok * p.lda + (int64_t)h * D + 4 * d4) = v;
+}
+
+int device_cu_count() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        n > 0)
+        return n;
+    return 256;
+}
+
+template <int D, bool CAUSAL, bool PACK>
 tp_status_t run_attn(AttnParams p, hipStream_t stream) {
     constexpr int QB = 32 * kWQ;
-    const int nqb = (p.M + QB - 1) / QB;
-    // Causal: a query block's work grows with its index. Cutting the upper half of the
-    // blocks in two key ranges bounds every workgroup's share by about the longest
-    // whole block's half, so the grid drains evenly.
-    p.qsplit = CAUSAL && nqb >= 4 ? nqb / 2 : nqb;
-    p.nsu = (nqb - p.qsplit) * p.hq;
+    const int gq = p.hq / p.hk;
+    const int HM = PACK ? p.hk : p.hq;
+    const int rows = PACK ? p.M * gq : p.M;
+    const int nqb = (rows + QB - 1) / QB;
+    auto kend_of = [&](int b) {
+        const int last = PACK ? std::min(p.M - 1, ((b + 1) * QB - 1) / gq) : std::min(p.M - 1, (b + 1) * QB - 1);
+        return CAUSAL ? std::min(p.Nk, p.pos0 + last + 1) : p.Nk;
+    };
+    // Cutting keys: causal prefill, where a query block's work grows with its index, cuts
+    // the blocks longer than half the longest in two, which bounds every workgroup's share;
+    // few query blocks (decode) cut their keys so that the grid has about two workgroups
+    // per CU, at least 4 key blocks each.
+    const int nkb_max = (kend_of(nqb - 1) + KB - 1) / KB;
+    p.L = 0;
+    if (PACK) {
+        // About one workgroup per CU, at most 128 ranges per query block (the merge reads
+        // up to 16 ranges per thread).
+        const int want = std::min(128, std::max(1, (device_cu_count() + nqb * HM - 1) / (nqb * HM)));
+        p.L = std::max(1, (nkb_max + want - 1) / want);
+        if (p.L >= nkb_max) p.L = 0;
+    } else if (CAUSAL && nqb >= 4) {
+        p.L = (nkb_max + 1) / 2;
+    }
     p.ws = nullptr;
     p.counters = nullptr;
-    if (p.nsu > 0) {
+    int64_t pieces = nqb;
+    if (p.L > 0) {
+        pieces = 0;
+        for (int b = 0; b < nqb; ++b) pieces += ((kend_of(b) - 1) / KB + p.L) / p.L;
+        // Partials: without PACK one slot of WQ x 64 lanes x (D/2 + 2) floats per workgroup;
+        // with PACK 128 rows x (D + 2) floats.
+        const size_t floats = (size_t)(pieces * HM) * (PACK ? QB * (D + 2) : kWQ * 64 * (D / 2 + 2));
         Workspace ws;
-        const tp_status_t st = get_workspace(stream, (size_t)p.nsu * 2 * kWQ * 64 * (D / 2 + 2), (size_t)p.nsu, &ws);
+        const tp_status_t st = get_workspace(stream, floats, (size_t)nqb * HM, &ws);
         if (st != TP_OK) return st;
         p.ws = ws.partials;
         p.counters = ws.counters;
+        p.ml_off = (int64_t)pieces * HM * QB * D;
     }
-    hipLaunchKernelGGL((attn_kernel<D, CAUSAL, kWQ>), dim3((unsigned)(2 * p.nsu + p.qsplit * p.hq)), dim3(128 * kWQ), 0,
+    hipLaunchKernelGGL((attn_kernel<D, CAUSAL, PACK, kWQ>), dim3((unsigned)(pieces * HM)), dim3(128 * kWQ), 0,
                        stream, p);
+    if (PACK && p.L > 0) {
+        const tp_status_t st = hip_status();
+        if (st != TP_OK) return st;
+        hipLaunchKernelGGL((attn_merge_kernel<D>), dim3((unsigned)(nqb * HM * QB)), dim3(256), 0, stream, p, nqb);
+    }
     return hip_status();
+}
+
+template <bool PACK>
+tp_status_t run_attn_d(const AttnParams& p, int d, bool causal, hipStream_t stream) {
+    if (d == 128) return causal ? run_attn<128, true, PACK>(p, stream) : run_attn<128, false, PACK>(p, stream);
+    if (d == 64) return causal ? run_attn<64, true, PACK>(p, stream) : run_attn<64, false, PACK>(p, stream);
+    return TP_ERR_SHAPE;
 }
 
 }  // namespace
 
 tp_status_t launch_attn_core(const void* qkv, int64_t ldq, void* out, int64_t lda, int64_t M, int hq, int hk, int d,
                              bool causal, hipStream_t stream) {
+    // Buffer offsets are 32-bit: the K and V column blocks must lie within 2 GiB.
+    if (M * ldq * 2 >= (int64_t(1) << 31)) return TP_ERR_SHAPE;
     AttnParams p;
-    p.qkv = static_cast<const bf16*>(qkv);
-    p.ldq = ldq;
+    const bf16* base = static_cast<const bf16*>(qkv);
+    p.q = base;
+    p.k = base + (int64_t)hq * d;
+    p.v = base + (int64_t)(hq + hk) * d;
     p.out = static_cast<bf16*>(out);
+    p.ldq = p.ldk = p.ldv = ldq;
     p.lda = lda;
-    p.M = (int)M;
+    p.M = p.Nk = (int)M;
+    p.pos0 = 0;
     p.hq = hq;
     p.hk = hk;
     p.scale_log2 = 1.4426950408889634f / sqrtf((float)d);
-    // Buffer offsets are 32-bit: the K and V column blocks must lie within 2 GiB.
-    if (M * ldq * 2 >= (int64_t(1) << 31)) return TP_ERR_SHAPE;
-    if (d == 128) return causal ? run_attn<128, true>(p, stream) : run_attn<128, false>(p, stream);
-    if (d == 64) return causal ? run_attn<64, true>(p, stream) : run_attn<64, false>(p, stream);
-    return TP_ERR_SHAPE;
+    return run_attn_d<false>(p, d, causal, stream);
+}
+
+tp_status_t launch_attn_decode(const void* qkv, int64_t ldq, const void* kc, const void* vc, int64_t ldkv,
+                               int64_t n_keys, void* out, int64_t lda, int64_t M, int hq, int hk, int d,
+                               hipStream_t stream) {
+    if (n_keys * ldkv * 2 >= (int64_t(1) << 31)) return TP_ERR_SHAPE;
+    AttnParams p;
+    p.q = static_cast<const bf16*>(qkv);
+    p.k = static_cast<const bf16*>(kc);
+    p.v = static_cast<const bf16*>(vc);
+    p.out = static_cast<bf16*>(out);
+    p.ldq = ldq;
+    p.ldk = p.ldv = ldkv;
+    p.lda = lda;
+    p.M = (int)M;
+    p.Nk = (int)n_keys;
+    p.pos0 = (int)(n_keys - M);
+    p.hq = hq;
+    p.hk = hk;
+    p.scale_log2 = 1.4426950408889634f / sqrtf((float)d);
+    return run_attn_d<true>(p, d, true, stream);
 }
 
 }  // namespace tp

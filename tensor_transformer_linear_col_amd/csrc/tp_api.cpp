@@ -251,6 +251,35 @@ tp_status_t tp_attn_core_shard(const void* QKV_r, void* A_r, int64_t M, int32_t 
                             static_cast<hipStream_t>(stream));
 }
 
+tp_status_t tp_attn_decode_shard(const void* QKV_r, void* K_cache_r, void* V_cache_r, int64_t cache_len,
+                                 int64_t capacity, void* A_r, int64_t M, int32_t n_heads, int32_t n_kv_heads,
+                                 int32_t head_dim, int32_t tp_size, tp_dtype_t dtype, void* stream) {
+    if (!QKV_r || !K_cache_r || !V_cache_r || !A_r) return TP_ERR_NULL;
+    if (dtype != TP_DTYPE_BF16) return TP_ERR_DTYPE;
+    TP_TRY(check_dims(M, {n_heads, n_kv_heads}));
+    if (tp_size < 1 || tp_size > kMaxTP) return TP_ERR_SHAPE;
+    if (head_dim != 64 && head_dim != 128) return TP_ERR_SHAPE;
+    if (cache_len < 0 || capacity < 0 || capacity > kMaxDim || cache_len + M > capacity) return TP_ERR_SHAPE;
+    if (n_heads % tp_size != 0 || kv_heads_per_shard(n_kv_heads, tp_size) == 0) return TP_ERR_INDIVISIBLE;
+    const int64_t hq = n_heads / tp_size, hk = kv_heads_per_shard(n_kv_heads, tp_size);
+    if (hq % hk != 0) return TP_ERR_INDIVISIBLE;
+    const int64_t ldq = (hq + 2 * hk) * head_dim, ldkv = hk * head_dim, lda = hq * head_dim;
+    TP_TRY(check_vec_operand(QKV_r, ldq, dtype));
+    TP_TRY(check_vec_operand(K_cache_r, ldkv, dtype));
+    TP_TRY(check_vec_operand(V_cache_r, ldkv, dtype));
+    TP_TRY(check_vec_operand(A_r, lda, dtype));
+    if (M == 0) return TP_OK;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    // Append the new tokens' K and V rows at positions cache_len .. cache_len + M - 1.
+    const char* qkv = static_cast<const char*>(QKV_r);
+    TP_TRY(launch_copy2d(qkv + hq * head_dim * 2, ldq, static_cast<char*>(K_cache_r) + cache_len * ldkv * 2, ldkv, M,
+                         ldkv, 2, st));
+    TP_TRY(launch_copy2d(qkv + (hq + hk) * head_dim * 2, ldq, static_cast<char*>(V_cache_r) + cache_len * ldkv * 2,
+                         ldkv, M, ldkv, 2, st));
+    return launch_attn_decode(QKV_r, ldq, K_cache_r, V_cache_r, ldkv, cache_len + M, A_r, lda, M, (int)hq, (int)hk,
+                              head_dim, st);
+}
+
 tp_status_t tp_combine_concat(const void* const* shards, int32_t tp_size, const int64_t* seg_widths, int32_t nseg,
                               void* Y, int64_t M, tp_dtype_t dtype, void* stream) {
     if (!shards || !seg_widths || !Y) return TP_ERR_NULL;

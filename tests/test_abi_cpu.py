@@ -31,7 +31,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     for name in names:
         assert hasattr(L, name), name
     assert set(names) == set(tp.EXPORTS)
@@ -150,6 +150,23 @@ def test_attn_core_shard_errors(L):
     assert core(Q=P + 8) == ALIGN
     assert core(M=0) == OK
     assert core(M=0, nkv=8, p=16) == OK              # KV heads replicated
+
+
+def test_attn_decode_shard_errors(L):
+    dec = lambda **k: L.tp_attn_decode_shard(k.get("Q", P), k.get("Kc", P), k.get("Vc", P), k.get("T", 100),
+                                             k.get("cap", 4096), k.get("A", P), k.get("M", 1), k.get("nh", 64),
+                                             k.get("nkv", 8), k.get("d", 128), k.get("p", 8), k.get("dt", BF16), None)
+    assert dec(Kc=0) == NULL
+    assert dec(Vc=0) == NULL
+    assert dec(dt=F32) == DTYPE
+    assert dec(d=80) == SHAPE
+    assert dec(T=-1) == SHAPE
+    assert dec(T=4096, M=1) == SHAPE                 # no room left in the cache
+    assert dec(T=4000, M=97) == SHAPE
+    assert dec(p=3) == INDIV
+    assert dec(Kc=P + 8) == ALIGN
+    assert dec(M=0) == OK                            # nothing to append or attend
+    assert dec(M=0, T=4096) == OK
 
 
 def test_attn_proj_shard_errors(L):

@@ -87,3 +87,59 @@ def test_attention_chain_qkv_core_o():
     qkv = O.linear(host64(x), w64["Wqkv"], w64["bqkv"])
     a = O.attention_core_shard(qkv, nh, nkv, d, True)
     assert err(Y, O.linear(a, w64["Wo"], w64["bo"])) <= BF16_TOL
+
+
+def _decode_sequence(S, nh, nkv, d, p, chunks, seed, capacity=None):
+    """Feed a seeded S-token sequence of one shard's QKV rows through tp_attn_decode_shard in
+    the given chunks; check every chunk's A_r against the rows of the oracle's causal pass over
+    the whole sequence, and the caches against the sequence's K and V columns."""
+    hq, hk = nh // p, tp.kv_heads_per_shard(nkv, p)
+    qkv = I.activations(S, (hq + 2 * hk) * d, seed)
+    full = O.attention_core_shard(host64(qkv), hq, hk, d, True)
+    cap = capacity or S
+    Kc = torch.zeros(cap, hk * d, dtype=torch.bfloat16, device="cuda")
+    Vc = torch.zeros(cap, hk * d, dtype=torch.bfloat16, device="cuda")
+    Q = dev(qkv)
+    t = 0
+    for m in chunks:
+        log_case("attention decode", S, nh, nkv, d, p, t, m)
+        buf, A = canary_buffer((m, hq * d), torch.bfloat16)
+        tp.tp_attn_decode_shard(Q[t:t + m], Kc, Vc, t, A, m, nh, nkv, d, p)
+        torch.cuda.synchronize()
+        assert err(A, full[t:t + m]) <= BF16_TOL, (t, m)
+        assert canaries_intact(buf, (m, hq * d))
+        t += m
+    assert torch.equal(Kc[:t].cpu(), qkv[:t, hq * d:(hq + hk) * d])
+    assert torch.equal(Vc[:t].cpu(), qkv[:t, (hq + hk) * d:])
+
+
+def test_attention_decode_70b_shard_over_cache():
+    """70B at TP = 8 (8 query heads share 1 KV head of 128): a 300-token prompt through the
+    cache, then single tokens and short chunks; the grouped heads are packed into one
+    workgroup's rows."""
+    _decode_sequence(400, 64, 8, 128, 8, [300, 1, 1, 7, 64, 27], 640, capacity=512)
+
+
+def test_attention_decode_long_cache_cut_keys():
+    """A 2000-token cache with 2 KV heads of 64: the keys are cut into ranges merged through the
+    work space (one and sixteen new tokens)."""
+    _decode_sequence(2033, 8, 4, 64, 2, [2000, 1, 16, 16], 650)
+
+
+def test_attention_decode_prompt_equals_core():
+    """An empty cache and the whole prompt in one call: the same attention as the core."""
+    M, nh, nkv, d, p = 777, 32, 8, 128, 4
+    hq, hk = nh // p, nkv // p
+    qkv = I.activations(M, (hq + 2 * hk) * d, 660)
+    Q = dev(qkv)
+    A1 = torch.empty(M, hq * d, dtype=torch.bfloat16, device="cuda")
+    A2 = torch.empty(M, hq * d, dtype=torch.bfloat16, device="cuda")
+    Kc = torch.zeros(M, hk * d, dtype=torch.bfloat16, device="cuda")
+    Vc = torch.zeros(M, hk * d, dtype=torch.bfloat16, device="cuda")
+    log_case("attention decode prompt", M, nh, nkv, d, p)
+    tp.tp_attn_core_shard(Q, A1, M, nh, nkv, d, p, True)
+    tp.tp_attn_decode_shard(Q, Kc, Vc, 0, A2, M, nh, nkv, d, p)
+    torch.cuda.synchronize()
+    ref = O.attention_core_shard(host64(qkv), hq, hk, d, True)
+    assert err(A1, ref) <= BF16_TOL
+    assert err(A2, ref) <= BF16_TOL

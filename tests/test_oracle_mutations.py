@@ -122,6 +122,35 @@ def _attn_variant(qkv_r, hq, hk, d, causal, scale, mask):
     return out
 
 
+def _decode_excludes_self(qkv_new, k_cache, v_cache, hq, hk, d):
+    return _decode_variant(qkv_new, k_cache, v_cache, hq, hk, d, 0)
+
+
+def _decode_cache_only(qkv_new, k_cache, v_cache, hq, hk, d):
+    return _decode_variant(qkv_new, k_cache, v_cache, hq, hk, d, None)
+
+
+def _decode_variant(qkv_new, k_cache, v_cache, hq, hk, d, shift):
+    """shift 0: token i sees keys j < T + i (the new tokens before it, not itself); None: only
+    the cache (as if the new rows were appended after the attention). Key 0 always stays
+    allowed so that no row is empty."""
+    qkv_new, k_cache, v_cache = T.f64(qkv_new), T.f64(k_cache), T.f64(v_cache)
+    m, t = qkv_new.shape[0], k_cache.shape[0]
+    k_all = np.concatenate([k_cache, qkv_new[:, hq * d:(hq + hk) * d]], axis=0)
+    v_all = np.concatenate([v_cache, qkv_new[:, (hq + hk) * d:(hq + 2 * hk) * d]], axis=0)
+    keys = np.arange(t + m)[None, :]
+    limit = (t + np.arange(m))[:, None] if shift is not None else np.full((m, 1), t)
+    allowed = (keys < limit) | (keys == 0)
+    out = np.zeros((m, hq * d))
+    for h in range(hq):
+        g = h // (hq // hk)
+        q, k, v = qkv_new[:, h * d:(h + 1) * d], k_all[:, g * d:(g + 1) * d], v_all[:, g * d:(g + 1) * d]
+        s = np.where(allowed, (q @ k.T) / np.sqrt(d), -np.inf)
+        e = np.exp(s - s.max(axis=1, keepdims=True))
+        out[:, h * d:(h + 1) * d] = (e / e.sum(axis=1, keepdims=True)) @ v
+    return out, k_all, v_all
+
+
 MUTATIONS = [
     ("linear", _linear_no_bias, [P.test_toy_full_output_matches_printed_values]),
     ("linear", _linear_bias_twice, [P.test_toy_full_output_matches_printed_values,
@@ -141,6 +170,10 @@ MUTATIONS = [
     ("attention_core_shard", _attention_no_mask, [P.test_attention_uniform_scores_give_prefix_means,
                                                   P.test_attention_first_causal_row_and_dominant_key]),
     ("kv_heads_of", _kv_heads_of_no_replication, [P.test_kv_heads_replicated_when_more_shards_than_kv_heads]),
+    ("attention_decode_shard", _decode_excludes_self, [P.test_attention_decode_over_cache_equals_the_full_causal_pass,
+                                                       P.test_attention_decode_single_token_by_bruteforce]),
+    ("attention_decode_shard", _decode_cache_only, [P.test_attention_decode_over_cache_equals_the_full_causal_pass,
+                                                    P.test_attention_decode_single_token_by_bruteforce]),
 ]
 
 

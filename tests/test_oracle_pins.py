@@ -302,6 +302,40 @@ def test_attention_shards_equal_unsharded_heads():
         np.testing.assert_allclose(a_r, full[:, r * (nh // p) * d:(r + 1) * (nh // p) * d], rtol=1e-12, atol=1e-14)
 
 
+def test_attention_decode_over_cache_equals_the_full_causal_pass():
+    """Causality: a token's output does not depend on later tokens, so feeding a sequence in
+    chunks through the cache gives the rows of one causal pass over the whole sequence; the
+    cache ends up holding exactly the sequence's K and V columns."""
+    m, hq, hk, d = 11, 4, 2, 8
+    qkv = _qkv(m, hq, hk, d, 65)
+    full = O.attention_core_shard(qkv, hq, hk, d, causal=True)
+    kc = np.zeros((0, hk * d))
+    vc = np.zeros((0, hk * d))
+    t = 0
+    for chunk in (4, 1, 1, 5):
+        a, kc, vc = O.attention_decode_shard(qkv[t:t + chunk], kc, vc, hq, hk, d)
+        np.testing.assert_allclose(a, full[t:t + chunk], rtol=1e-12, atol=1e-14)
+        t += chunk
+    np.testing.assert_array_equal(kc, qkv[:, hq * d:(hq + hk) * d])
+    np.testing.assert_array_equal(vc, qkv[:, (hq + hk) * d:])
+
+
+def test_attention_decode_single_token_by_bruteforce():
+    """One new token over a 3-row cache: explicit fsum loops over its 4 allowed keys."""
+    hq, hk, d, t = 2, 1, 3, 3
+    qkv = _qkv(t + 1, hq, hk, d, 66)
+    kc, vc = qkv[:t, hq * d:(hq + hk) * d], qkv[:t, (hq + hk) * d:]
+    a, _, _ = O.attention_decode_shard(qkv[t:], kc, vc, hq, hk, d)
+    for h in range(hq):
+        sc = [math.fsum(qkv[t, h * d + x] * qkv[j, hq * d + x] for x in range(d)) / math.sqrt(d) for j in range(t + 1)]
+        mx = max(sc)
+        w = [math.exp(c - mx) for c in sc]
+        z = math.fsum(w)
+        for x in range(d):
+            o = math.fsum(w[j] * qkv[j, (hq + hk) * d + x] for j in range(t + 1)) / z
+            assert abs(a[0, h * d + x] - o) <= 1e-13 * max(1.0, abs(o))
+
+
 def test_indivisible_sizes_are_rejected():
     w = np.zeros((10, 9))
     with pytest.raises(ValueError):
