@@ -1,11 +1,16 @@
 // Head-local attention core of one shard: A_r = [O_0 | O_1 | ...] with
 //   O_h = softmax(Q_h K_g^T / sqrt(d), causal mask) V_g,  g = h / (hq / hk),
-// read straight out of the shard's QKV_r ([M, (hq + 2 hk) d], segments Q | K | V).
+// read straight out of the shard's QKV_r ([M, (hq + 2 hk) d], segments Q | K | V), or,
+// for a decode step, with K and V from the shard's cache (the new tokens at the end).
 // Heads go to different GPUs ("What is tensor parallelism?", section "How a layer is
 // split"), so the core needs nothing from other shards; its formula is not on the
 // pages (scaled dot-product attention, causal, grouped-query: a reading).
 //
-// One workgroup = 8 waves = 128 query rows of one query head. Waves w and w + 4 own the
+// One workgroup = 8 waves = 128 query rows: 128 tokens of one query head (prefill), or
+// (token, head) pairs of one KV group (decode: the group's heads share every K/V block).
+// The keys of long query blocks are cut into ranges of their own workgroups whose
+// partial results are merged afterwards (by the last to arrive, or by a merge kernel).
+// Waves w and w + 4 own the
 // same 32 queries and split every 64-key block between them (keys 0..31 and 32..63 of
 // the block), each with its own running maximum, sum and output accumulators; the two
 // halves are merged once at the end. Two waves per SIMD let one wave's softmax run
