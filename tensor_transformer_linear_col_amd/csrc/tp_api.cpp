@@ -268,6 +268,8 @@ tp_status_t tp_attn_decode_shard(const void* QKV_r, void* K_cache_r, void* V_cac
     TP_TRY(check_vec_operand(K_cache_r, ldkv, dtype));
     TP_TRY(check_vec_operand(V_cache_r, ldkv, dtype));
     TP_TRY(check_vec_operand(A_r, lda, dtype));
+    // The kernel addresses the used part of a cache with 32-bit byte offsets.
+    if ((cache_len + M) * ldkv * 2 >= (int64_t(1) << 31)) return TP_ERR_SHAPE;
     if (M == 0) return TP_OK;
     const hipStream_t st = static_cast<hipStream_t>(stream);
     // Append the new tokens' K and V rows at positions cache_len .. cache_len + M - 1.

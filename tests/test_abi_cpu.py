@@ -165,6 +165,7 @@ def test_attn_decode_shard_errors(L):
     assert dec(T=4000, M=97) == SHAPE
     assert dec(p=3) == INDIV
     assert dec(Kc=P + 8) == ALIGN
+    assert dec(nkv=64, p=64, nh=64, T=1 << 23, cap=(1 << 23) + 8, M=1) == SHAPE  # 2 GiB of cache
     assert dec(M=0) == OK                            # nothing to append or attend
     assert dec(M=0, T=4096) == OK
 
