@@ -143,3 +143,49 @@ def test_attention_decode_prompt_equals_core():
     ref = O.attention_core_shard(host64(qkv), hq, hk, d, True)
     assert err(A1, ref) <= BF16_TOL
     assert err(A2, ref) <= BF16_TOL
+
+
+_RNG_CASES = [  # (M, hq, hk, d, causal): seeded draws of token counts over the head layouts
+    (m, hq, hk, d, causal)
+    for (m, (hq, hk), d, causal) in zip(
+        [3, 77, 191, 256, 385, 449, 640, 703],
+        [(2, 1), (4, 2), (8, 1), (6, 3), (8, 2), (2, 2), (12, 4), (8, 1)],
+        [64, 128, 128, 64, 128, 64, 128, 64],
+        [True, False, True, True, False, True, True, False])
+]
+
+
+@pytest.mark.parametrize("M,hq,hk,d,causal", _RNG_CASES)
+def test_attention_core_head_layouts(M, hq, hk, d, causal):
+    log_case("attention core layout", M, hq, hk, d, causal)
+    qkv = I.activations(M, (hq + 2 * hk) * d, 700 + M)
+    buf, A = _core(qkv, M, hq, hk, d, causal)
+    assert err(A, O.attention_core_shard(host64(qkv), hq, hk, d, causal)) <= BF16_TOL
+    assert canaries_intact(buf, (M, hq * d))
+
+
+@pytest.mark.parametrize("T,M,hq,hk,d", [(0, 5, 4, 4, 64), (17, 3, 6, 2, 128), (640, 200, 8, 1, 128),
+                                         (1500, 40, 4, 2, 64)])
+def test_attention_decode_shapes_and_determinism(T, M, hq, hk, d):
+    """One step of M new tokens over a T-token cache: the oracle's rows, the appended cache rows,
+    and a second identical call giving identical bits."""
+    log_case("attention decode step", T, M, hq, hk, d)
+    qkv = I.activations(T + M, (hq + 2 * hk) * d, 720 + T + M)
+    Q = dev(qkv)
+    full = O.attention_core_shard(host64(qkv), hq, hk, d, True)
+    outs = []
+    for _ in range(2):
+        Kc = torch.zeros(T + M + 8, hk * d, dtype=torch.bfloat16, device="cuda")
+        Vc = torch.zeros(T + M + 8, hk * d, dtype=torch.bfloat16, device="cuda")
+        Kc[:T] = Q[:T, hq * d:(hq + hk) * d]
+        Vc[:T] = Q[:T, (hq + hk) * d:]
+        buf, A = canary_buffer((M, hq * d), torch.bfloat16)
+        tp.tp_attn_decode_shard(Q[T:], Kc, Vc, T, A, M, hq, hk, d, 1)
+        torch.cuda.synchronize()
+        assert canaries_intact(buf, (M, hq * d))
+        assert torch.equal(Kc[:T + M].cpu(), qkv[:, hq * d:(hq + hk) * d])
+        assert torch.equal(Vc[:T + M].cpu(), qkv[:, (hq + hk) * d:])
+        assert not Kc[T + M:].any().item()  # nothing past the new rows
+        outs.append(A.clone())
+    assert err(outs[0], full[T:]) <= BF16_TOL
+    assert torch.equal(outs[0], outs[1])
