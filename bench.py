@@ -226,7 +226,7 @@ def attention_decode_bench(reps=50):
             gbs = (T + M) * 2 * hk * d * 2 / (us * 1e-6) / 1e9
             log(f"attention decode T={T} M={M}: {us:.1f} us, {gbs:.0f} GB/s")
             out.append({"cache_len": T, "M": M, "us": round(us, 2), "GB_s": round(gbs, 1)})
-    return {"kernels": "copy2d_kernel x2 (append K, V) + attn_kernel (packed query heads, cut keys)", "steps": out}
+    return {"kernels": "append_kv_kernel + attn_kernel (packed query heads, cut keys) + attn_merge_kernel", "steps": out}
 
 
 def kernel_ms(ev):

@@ -488,6 +488,21 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p, int nqb) 
     *reinterpret_cast<bf16x4*>(p.out + (int64_t)tok * p.lda + (int64_t)h * D + 4 * d4) = v;
 }
 
+// Appends M new tokens' K and V rows (QKV columns hq*d.. and (hq+hk)*d.., hk*d wide each) to
+// the caches at row T, in 16-byte units: one grid-stride pass over both copies.
+__global__ __launch_bounds__(256) void append_kv_kernel(const bf16* qkv, int64_t ldq, int64_t koff, int64_t voff,
+                                                        bf16* kc, bf16* vc, int64_t ldkv, int64_t T, int64_t M) {
+    const int64_t per_row = ldkv / 8;  // 16-byte units per cache row
+    const int64_t total = 2 * M * per_row;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+        const int64_t which = i / (M * per_row), j = i - which * M * per_row;
+        const int64_t r = j / per_row, u = j - r * per_row;
+        const bf16* src = qkv + r * ldq + (which ? voff : koff) + 8 * u;
+        bf16* dst = (which ? vc : kc) + (T + r) * ldkv + 8 * u;
+        *reinterpret_cast<bf16x8*>(dst) = *reinterpret_cast<const bf16x8*>(src);
+    }
+}
+
 int device_cu_count() {
     int dev = 0, n = 0;
     if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
@@ -577,10 +592,17 @@ tp_status_t launch_attn_core(const void* qkv, int64_t ldq, void* out, int64_t ld
     return run_attn_d<false>(p, d, causal, stream);
 }
 
-tp_status_t launch_attn_decode(const void* qkv, int64_t ldq, const void* kc, const void* vc, int64_t ldkv,
-                               int64_t n_keys, void* out, int64_t lda, int64_t M, int hq, int hk, int d,
-                               hipStream_t stream) {
+tp_status_t launch_attn_decode(const void* qkv, int64_t ldq, void* kc, void* vc, int64_t ldkv, int64_t cache_len,
+                               void* out, int64_t lda, int64_t M, int hq, int hk, int d, hipStream_t stream) {
+    const int64_t n_keys = cache_len + M;
     if (n_keys * ldkv * 2 >= (int64_t(1) << 31)) return TP_ERR_SHAPE;
+    const int64_t units = 2 * M * (ldkv / 8);
+    const unsigned grid = (unsigned)std::min<int64_t>((units + 255) / 256, 4096);
+    hipLaunchKernelGGL(append_kv_kernel, dim3(grid), dim3(256), 0, stream, static_cast<const bf16*>(qkv), ldq,
+                       (int64_t)hq * d, (int64_t)(hq + hk) * d, static_cast<bf16*>(kc), static_cast<bf16*>(vc), ldkv,
+                       cache_len, M);
+    const tp_status_t st = hip_status();
+    if (st != TP_OK) return st;
     AttnParams p;
     p.q = static_cast<const bf16*>(qkv);
     p.k = static_cast<const bf16*>(kc);
@@ -591,7 +613,7 @@ tp_status_t launch_attn_decode(const void* qkv, int64_t ldq, const void* kc, con
     p.lda = lda;
     p.M = (int)M;
     p.Nk = (int)n_keys;
-    p.pos0 = (int)(n_keys - M);
+    p.pos0 = (int)cache_len;
     p.hq = hq;
     p.hk = hk;
     p.scale_log2 = 1.4426950408889634f / sqrtf((float)d);

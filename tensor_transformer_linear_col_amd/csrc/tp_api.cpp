@@ -271,15 +271,8 @@ tp_status_t tp_attn_decode_shard(const void* QKV_r, void* K_cache_r, void* V_cac
     // The kernel addresses the used part of a cache with 32-bit byte offsets.
     if ((cache_len + M) * ldkv * 2 >= (int64_t(1) << 31)) return TP_ERR_SHAPE;
     if (M == 0) return TP_OK;
-    const hipStream_t st = static_cast<hipStream_t>(stream);
-    // Append the new tokens' K and V rows at positions cache_len .. cache_len + M - 1.
-    const char* qkv = static_cast<const char*>(QKV_r);
-    TP_TRY(launch_copy2d(qkv + hq * head_dim * 2, ldq, static_cast<char*>(K_cache_r) + cache_len * ldkv * 2, ldkv, M,
-                         ldkv, 2, st));
-    TP_TRY(launch_copy2d(qkv + (hq + hk) * head_dim * 2, ldq, static_cast<char*>(V_cache_r) + cache_len * ldkv * 2,
-                         ldkv, M, ldkv, 2, st));
-    return launch_attn_decode(QKV_r, ldq, K_cache_r, V_cache_r, ldkv, cache_len + M, A_r, lda, M, (int)hq, (int)hk,
-                              head_dim, st);
+    return launch_attn_decode(QKV_r, ldq, K_cache_r, V_cache_r, ldkv, cache_len, A_r, lda, M, (int)hq, (int)hk,
+                              head_dim, static_cast<hipStream_t>(stream));
 }
 
 tp_status_t tp_combine_concat(const void* const* shards, int32_t tp_size, const int64_t* seg_widths, int32_t nseg,

@@ -49,12 +49,11 @@ tp_status_t launch_f32(const LinearDesc& d, hipStream_t stream);
 // Head-local attention core: out[M, hq*d] (row stride lda) from qkv[M, (hq+2hk)*d] (row stride ldq).
 tp_status_t launch_attn_core(const void* qkv, int64_t ldq, void* out, int64_t lda, int64_t M, int hq, int hk, int d,
                              bool causal, hipStream_t stream);
-// Attention of M new tokens (positions n_keys - M ..) over n_keys cached keys and values:
-// q rows from qkv[M, ldq] (Q segment first), K and V rows kc/vc[n_keys, ldkv] (KV head g at
-// column g*d); causal; out[M, hq*d] (row stride lda).
-tp_status_t launch_attn_decode(const void* qkv, int64_t ldq, const void* kc, const void* vc, int64_t ldkv,
-                               int64_t n_keys, void* out, int64_t lda, int64_t M, int hq, int hk, int d,
-                               hipStream_t stream);
+// One decode step: appends the M new tokens' K and V rows of qkv[M, ldq] (Q segment first) to
+// the caches kc/vc[.., ldkv] at row cache_len, then attention of the new tokens (positions
+// cache_len ..) over cache_len + M keys, causal; out[M, hq*d] (row stride lda).
+tp_status_t launch_attn_decode(const void* qkv, int64_t ldq, void* kc, void* vc, int64_t ldkv, int64_t cache_len,
+                               void* out, int64_t lda, int64_t M, int hq, int hk, int d, hipStream_t stream);
 
 tp_status_t launch_combine_sum(const void* const* partials, int p, tp_dtype_t pdt, const void* b,
                                void* Y, int64_t M, int64_t N, tp_dtype_t odt, hipStream_t stream);
