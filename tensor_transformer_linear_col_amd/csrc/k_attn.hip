@@ -36,6 +36,7 @@
 // O^T registers hold one query per lane, so the rescale, the merge and the final 1/l
 // are per-lane scalars. Softmax and accumulation are fp32; A_r is rounded once to bf16.
 #include <algorithm>
+#include <vector>
 #include <type_traits>
 
 #include "tp_internal.h"
@@ -68,6 +69,12 @@ struct AttnParams {
     float* ws;          // one partial slot per workgroup (indexed like blockIdx)
     unsigned* counters; // one arrival counter per query block (without PACK)
     int64_t ml_off;
+    // Without PACK and with cut blocks: the workgroups' (query block, range) pairs, largest
+    // range first (entry = 4 * block + range; heads are the minor index of blockIdx), so
+    // the hardware's in-order dispatch schedules the longest work first. nord = 0: the
+    // order of the scalar walk below.
+    int nord;
+    unsigned short ord[768];
 };
 
 constexpr int KB = 64;  // keys per block
@@ -130,7 +137,13 @@ __global__ __launch_bounds__(128 * WQ, 2) void attn_kernel(AttnParams p) {
     // one, in key order. base = the first piece of this query block.
     const int hm = blockIdx.x % HM;
     int qblk, np = 1, part = 0, base = 0;
-    {
+    if (!PACK && p.nord > 0) {
+        const int e = p.ord[blockIdx.x / HM];
+        qblk = e >> 2;
+        part = e & 3;
+        np = (kend_of(qblk) - 1) / KB / p.L + 1;  // ceil(nkb / L)
+        base = 4 * qblk;                           // partial slots: four per query block
+    } else {
         int b = blockIdx.x / HM;
         if (p.L > 0) {
             // A scalar walk over the query blocks; its length grows like L, i.e. like the
@@ -523,9 +536,9 @@ tp_status_t run_attn(AttnParams p, hipStream_t stream) {
         return CAUSAL ? std::min(p.Nk, p.pos0 + last + 1) : p.Nk;
     };
     // Cutting keys: causal prefill, where a query block's work grows with its index, cuts
-    // the blocks longer than half the longest in two, which bounds every workgroup's share;
-    // few query blocks (decode) cut their keys so that the grid has about two workgroups
-    // per CU, at least 4 key blocks each.
+    // every block into ranges of at most a third of the longest, which bounds every
+    // workgroup's share (the ranges then run largest first, see ord); few query blocks
+    // (decode) cut their keys so that the grid has about one workgroup per CU.
     const int nkb_max = (kend_of(nqb - 1) + KB - 1) / KB;
     p.L = 0;
     if (PACK) {
@@ -535,7 +548,7 @@ tp_status_t run_attn(AttnParams p, hipStream_t stream) {
         p.L = std::max(1, (nkb_max + want - 1) / want);
         if (p.L >= nkb_max) p.L = 0;
     } else if (CAUSAL && nqb >= 4) {
-        p.L = (nkb_max + 1) / 2;
+        p.L = (nkb_max + 2) / 3;  // at most 3 ranges (measured: 2 and 4 ranges are slower)
     }
     p.ws = nullptr;
     p.counters = nullptr;
@@ -545,13 +558,30 @@ tp_status_t run_attn(AttnParams p, hipStream_t stream) {
         for (int b = 0; b < nqb; ++b) pieces += ((kend_of(b) - 1) / KB + p.L) / p.L;
         // Partials: without PACK one slot of WQ x 64 lanes x (D/2 + 2) floats per workgroup;
         // with PACK 128 rows x (D + 2) floats.
-        const size_t floats = (size_t)(pieces * HM) * (PACK ? QB * (D + 2) : kWQ * 64 * (D / 2 + 2));
+        const int64_t slots = PACK ? pieces : std::max<int64_t>(pieces, 4 * (int64_t)nqb);
+        const size_t floats = (size_t)(slots * HM) * (PACK ? QB * (D + 2) : kWQ * 64 * (D / 2 + 2));
         Workspace ws;
         const tp_status_t st = get_workspace(stream, floats, (size_t)nqb * HM, &ws);
         if (st != TP_OK) return st;
         p.ws = ws.partials;
         p.counters = ws.counters;
         p.ml_off = (int64_t)pieces * HM * QB * D;
+    }
+    // Causal prefill: largest ranges first (a cut block's halves are about half as long as
+    // an uncut block of the same index, so the plain walk would queue long uncut blocks
+    // behind short halves).
+    p.nord = 0;
+    if (!PACK && p.L > 0 && pieces <= (int64_t)(sizeof(p.ord) / sizeof(p.ord[0]))) {
+        struct Piece { int size, e; };
+        std::vector<Piece> v;
+        for (int b = nqb - 1; b >= 0; --b) {
+            const int nkb = (kend_of(b) - 1) / KB + 1;
+            const int np = (nkb - 1) / p.L + 1;
+            for (int q = 0; q < np; ++q) v.push_back({(q + 1) * nkb / np - q * nkb / np, 4 * b + q});
+        }
+        std::stable_sort(v.begin(), v.end(), [](const Piece& a, const Piece& b) { return a.size > b.size; });
+        for (size_t i = 0; i < v.size(); ++i) p.ord[i] = (unsigned short)v[i].e;
+        p.nord = (int)v.size();
     }
     hipLaunchKernelGGL((attn_kernel<D, CAUSAL, PACK, kWQ>), dim3((unsigned)(pieces * HM)), dim3(128 * kWQ), 0,
                        stream, p);
