@@ -1,11 +1,11 @@
 """Turn two rocprofv3 counter runs of bench.py into HBM bytes per launch of a kernel.
 
 Run from the repository root on one MI355X (each pass its own process):
-  rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/fetch -o p -- \\
+  rocprofv3 --pmc FETCH_SIZE --output-format csv -d prof/fetch -o p -- \\
       python bench.py --steps 2 --warmup 1 --skip-cpu-baseline --skip-decode --traffic-copy-mib 512
-  rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/write -o p -- \\
+  rocprofv3 --pmc WRITE_SIZE --output-format csv -d prof/write -o p -- \\
       python bench.py --steps 2 --warmup 1 --skip-cpu-baseline --skip-decode --traffic-copy-mib 512
-  python bench_traffic.py --fetch gpurun_out/fetch --write gpurun_out/write --copy-mib 512
+  python bench_traffic.py --fetch prof/fetch --write prof/write --copy-mib 512
 
 FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what each reads for the
 plain copy of known size that bench.py runs first (the copy2d dispatch with the

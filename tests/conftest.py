@@ -13,7 +13,7 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    """Skip GPU tests cleanly when no GPU is visible (they are run on the GPU machine)."""
+    """Skip GPU tests cleanly when no GPU is visible (they need an MI355X)."""
     try:
         import torch
         has_gpu = torch.cuda.is_available()
