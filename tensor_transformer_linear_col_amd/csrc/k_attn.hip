@@ -93,6 +93,18 @@ __device__ __forceinline__ bf16x8 load16(const void* base, uint32_t bytes, uint3
 #endif
 }
 
+// Max and sum of a value over the two lane halves that hold one query (lanes i and i ^ 32):
+// one cross-half swap of the register (lanes 0..31 then hold the upper half's values and
+// the others the lower half's) instead of an LDS permute. Both halves get the same bits.
+__device__ __forceinline__ float halves_max(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Storage position of key k of a block in the transposed V tile (see above).
 __device__ __forceinline__ int vpos(int k) {
     const int g = (k >> 2) & 3;
@@ -289,7 +301,7 @@ __global__ __launch_bounds__(128 * WQ, 2) void attn_kernel(AttnParams p) {
             float mx = -INFINITY;
 #pragma unroll
             for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[e]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            mx = halves_max(mx);
             // Raise m (and rescale) only when some query's maximum grew past the margin.
             if (__any(mx > m_run + thr)) {
                 const float m_new = fmaxf(m_run, mx);
@@ -331,7 +343,7 @@ __global__ __launch_bounds__(128 * WQ, 2) void attn_kernel(AttnParams p) {
 
     // Merge the two key halves: wave w + WQ leaves (m, l, O^T) in LDS, wave w combines.
     // Lane order in the merge area: [wave slice][register][lane], conflict-free.
-    l_run += __shfl_xor(l_run, 32);
+    l_run = halves_sum(l_run);
     __syncthreads();  // every wave is done with the block buffers
     float* mg = reinterpret_cast<float*>(lds) + wq * 64 * NR;
     if (kh == 1) {
