@@ -66,8 +66,8 @@ struct AttnParams {
     // next launch, merges them: O^T rows at ws[slot][row][d], (m, l) at ws[ml_off + (slot *
     // 128 + row) * 2].
     int L;
-    float* ws;          // one partial slot per workgroup (indexed like blockIdx)
-    unsigned* counters; // one arrival counter per query block (without PACK)
+    float* ws;          // partial slots: (slot of the range) * (heads or KV groups) + head or group
+    unsigned* counters; // one arrival counter per (query block, head) (without PACK)
     int64_t ml_off;
     // Without PACK and with cut blocks: the workgroups' (query block, range) pairs, largest
     // range first (entry = 4 * block + range; heads are the minor index of blockIdx), so
@@ -144,9 +144,10 @@ __global__ __launch_bounds__(128 * WQ, 2) void attn_kernel(AttnParams p) {
     auto last_tok = [&](int b) { return PACK ? min(p.M - 1, ((b + 1) * QB - 1) / gq) : min(p.M - 1, (b + 1) * QB - 1); };
     auto kend_of = [&](int b) { return CAUSAL ? min(p.Nk, p.pos0 + last_tok(b) + 1) : p.Nk; };
 
-    // Workgroup -> (head or KV group, query block, key range): blockIdx = piece * HM + hm,
-    // pieces enumerated from the last (longest, when causal) query block down and, within
-    // one, in key order. base = the first piece of this query block.
+    // Workgroup -> (head or KV group, query block, key range): blockIdx = piece * HM + hm.
+    // With an order table the piece is ord[blockIdx / HM] (slots: four per query block);
+    // otherwise pieces are enumerated from the last (longest, when causal) query block down
+    // and, within one, in key order (base = the slot of this query block's first piece).
     const int hm = blockIdx.x % HM;
     int qblk, np = 1, part = 0, base = 0;
     if (!PACK && p.nord > 0) {
