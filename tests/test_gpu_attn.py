@@ -189,3 +189,19 @@ def test_attention_decode_shapes_and_determinism(T, M, hq, hk, d):
         outs.append(A.clone())
     assert err(outs[0], full[T:]) <= BF16_TOL
     assert torch.equal(outs[0], outs[1])
+
+
+def test_attention_core_70b_shard_full_size():
+    """The size bench.py times: 8 query heads and 1 KV head of 128 over 4096 tokens, causal, in
+    its launch configuration (query blocks cut into up to 3 key ranges, largest first), against
+    the oracle on every element."""
+    M, nh, nkv, d, p = 4096, 64, 8, 128, 8
+    hq, hk = nh // p, nkv // p
+    log_case("attention core full size", M, hq, hk, d)
+    qkv = I.activations(M, (hq + 2 * hk) * d, 680)
+    Q = dev(qkv)
+    buf, A = canary_buffer((M, hq * d), torch.bfloat16)
+    tp.tp_attn_core_shard(Q, A, M, nh, nkv, d, p, True)
+    torch.cuda.synchronize()
+    assert err(A, O.attention_core_shard(host64(qkv), hq, hk, d, True)) <= BF16_TOL
+    assert canaries_intact(buf, (M, hq * d))
