@@ -205,3 +205,25 @@ def test_attention_core_70b_shard_full_size():
     torch.cuda.synchronize()
     assert err(A, O.attention_core_shard(host64(qkv), hq, hk, d, True)) <= BF16_TOL
     assert canaries_intact(buf, (M, hq * d))
+
+
+@pytest.mark.parametrize("T,M", [(4096, 1), (32768, 16)])
+def test_attention_decode_bench_sizes(T, M):
+    """The decode steps bench.py times (70B TP=8 shard: 8 query heads over 1 KV head of 128):
+    M new tokens over a T-token cache, against the oracle's decode step."""
+    nh, nkv, d, p = 64, 8, 128, 8
+    hq, hk = nh // p, nkv // p
+    log_case("attention decode bench size", T, M)
+    cache = I.activations(T, 2 * hk * d, 690 + M)
+    new = I.activations(M, (hq + 2 * hk) * d, 691 + M)
+    Kc = torch.zeros(T + M, hk * d, dtype=torch.bfloat16, device="cuda")
+    Vc = torch.zeros(T + M, hk * d, dtype=torch.bfloat16, device="cuda")
+    Kc[:T] = dev(cache[:, :hk * d])
+    Vc[:T] = dev(cache[:, hk * d:])
+    buf, A = canary_buffer((M, hq * d), torch.bfloat16)
+    tp.tp_attn_decode_shard(dev(new), Kc, Vc, T, A, M, nh, nkv, d, p)
+    torch.cuda.synchronize()
+    c64 = host64(cache)
+    ref, _, _ = O.attention_decode_shard(host64(new), c64[:, :hk * d], c64[:, hk * d:], hq, hk, d)
+    assert err(A, ref) <= BF16_TOL
+    assert canaries_intact(buf, (M, hq * d))
