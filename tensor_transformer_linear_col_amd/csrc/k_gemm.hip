@@ -266,7 +266,7 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_kernel(GemmParams p) {
 #define TP_DMA_STAGES 2
 #endif
 #ifndef TP_DMA_WAVES_M
-#define TP_DMA_WAVES_M 2
+#define TP_DMA_WAVES_M 4
 #endif
 #ifndef TP_DMA_SPREAD
 #define TP_DMA_SPREAD 2
@@ -420,11 +420,14 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void gemm_dtl_kernel(GemmPar
     // refills is a template flag, so no branch splits a sub-step and the interleaving
     // below holds for every slice.
     constexpr int NSPREAD = TP_DMA_SPREAD;
-    static_assert(NSPREAD >= 1 && NSPREAD <= KS && IPW % NSPREAD == 0, "DMA spread");
+    // The refill DMAs must all be issued before the last sub-step's wait for the next slice.
+    static_assert(NSPREAD >= 1 && NSPREAD < KS && IPW % NSPREAD == 0, "DMA spread");
     constexpr int NMF = NA * BM;                 // MFMAs per sub-step
     constexpr int NRD = NA + BM;                 // fragment reads per sub-step
     constexpr int DPS = IPW / NSPREAD;           // DMA instructions per spread sub-step
-    static_assert(NRD + DPS <= NMF, "one fragment read or DMA per MFMA");
+    static_assert(NRD <= NMF, "one fragment read per MFMA");
+    // DMAs that find no MFMA after the reads go behind the last one.
+    constexpr int DTAIL = NRD + DPS > NMF ? NRD + DPS - NMF : 0;
     bf16x8 fa0[NA], fb0[BM], fa1[NA], fb1[BM];
 
     // acc = the product over K slices kt0 .. kt0+nkt-1 of the tile whose rows goff holds.
@@ -475,6 +478,7 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void gemm_dtl_kernel(GemmPar
                     else if (REFILL && ks < NSPREAD && q - NRD < DPS)
                         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one DMA
                 }
+                if (REFILL && ks < NSPREAD && DTAIL > 0) __builtin_amdgcn_sched_group_barrier(0x020, DTAIL, 0);
                 __builtin_amdgcn_sched_barrier(0);
                 __builtin_amdgcn_s_waitcnt(kLgkm0);
             }
