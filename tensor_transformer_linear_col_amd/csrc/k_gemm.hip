@@ -265,9 +265,6 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_kernel(GemmParams p) {
 #ifndef TP_DMA_STAGES
 #define TP_DMA_STAGES 2
 #endif
-#ifndef TP_DMA_WAVES_M
-#define TP_DMA_WAVES_M 4
-#endif
 #ifndef TP_DMA_SPREAD
 #define TP_DMA_SPREAD 2
 #endif
@@ -775,17 +772,20 @@ tp_status_t launch_gemm(const LinearDesc& d, hipStream_t stream) {
             hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
             cus = n;
     }
-    // Large tiles (256 x 256, or 128 x 256 with the SwiGLU pair: 4 waves of 128 x 128
-    // outputs, one workgroup per CU) when they fill the chip; with K a whole number
-    // of slices they run on the LDS-DMA kernel, which also takes fewer tiles than CUs
-    // once each CU gets at least 16 slices of stream-K work. Otherwise 128 x 128
-    // tiles (4 waves of 64 x 64, two workgroups per CU).
+    // Large tiles (256 x 256, or 128 x 256 with the SwiGLU pair, one workgroup per CU)
+    // when they fill the chip; with K a whole number of slices they run on the LDS-DMA
+    // kernel with 8 waves of 128 x 64 outputs (SwiGLU: 16 waves of 32 pairs x 64), so a
+    // SIMD holds 2 (4) waves and one's MFMAs cover another's waits on the DMA and L2
+    // misses (measured in the layer step, where each shard's weights come cold from
+    // HBM: 907 -> 992 TFLOP/s over 4 waves of 128 x 128); the DMA kernel also takes
+    // fewer tiles than CUs once each CU gets at least 16 slices of split-K work.
+    // Otherwise register-staged 256 x 256 or 128 x 128 tiles.
     const bool dma = d.K % DBK == 0;
     const int64_t kt = d.K / DBK;
     if (d.swiglu) {
         const int64_t big = ceil_div(d.N, 128) * ceil_div(d.M, 256);
         if (dma && (big >= cus || big * kt >= 16 * (int64_t)cus))
-            return run_dtl_bias<128, 256, 2, TP_DMA_WAVES_M, kActSwiglu>(d, cus, stream);
+            return run_dtl_bias<128, 256, 4, 4, kActSwiglu>(d, cus, stream);
         if (big >= cus) return run_bias<128, 256, 2, 2, kActSwiglu>(d, stream);
         return run_bias<64, 128, 2, 2, kActSwiglu>(d, stream);
     }
@@ -793,7 +793,7 @@ tp_status_t launch_gemm(const LinearDesc& d, hipStream_t stream) {
     auto plain = [&](auto act) -> tp_status_t {
         constexpr int A = decltype(act)::value;
         if (dma && (big >= cus || big * kt >= 16 * (int64_t)cus))
-            return run_dtl_bias<256, 256, 2, TP_DMA_WAVES_M, A>(d, cus, stream);
+            return run_dtl_bias<256, 256, 2, 4, A>(d, cus, stream);
         if (big >= cus) return run_bias<256, 256, 2, 2, A>(d, stream);
         return run_bias<128, 128, 2, 2, A>(d, stream);
     };
