@@ -28,7 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNELS = {
     # name -> (substring of the mangled kernel name, source file)
     "gemm_gateup_swiglu_llama70b_tp8_m4096": (
-        "gemm_dtl_kernelILi128ELi256ELi2ELi2ELi1ELb1ELb0EDF16b",
+        "gemm_dtl_kernelILi128ELi256ELi4ELi4ELi1ELb1ELb0EDF16b",
         "tensor_transformer_linear_col_amd/csrc/k_gemm.hip"),
 }
 
