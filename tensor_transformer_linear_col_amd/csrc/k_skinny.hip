@@ -40,6 +40,12 @@
 #ifndef TP_SKINNY_U4
 #define TP_SKINNY_U4 2
 #endif
+#ifndef TP_SKINNY_M2
+#define TP_SKINNY_M2 5
+#endif
+#ifndef TP_SKINNY_M4G
+#define TP_SKINNY_M4G 3
+#endif
 
 namespace tp {
 namespace {
@@ -282,8 +288,9 @@ int device_cus() {
     return cached[dev];
 }
 
+// whole_k: never split K across workgroups (one workgroup per row group).
 template <int MT, int RT, int NW, int U, bool PERSIST, int ACT, bool BIAS, typename OutT>
-tp_status_t run(const LinearDesc& d, hipStream_t stream) {
+tp_status_t run(const LinearDesc& d, hipStream_t stream, bool whole_k = false) {
     constexpr int RH = ACT == kActSwiglu ? RT / 2 : RT;
     constexpr int KS = 32 * U;
     constexpr int TILEF = RT * MT * 4 * 64;
@@ -318,7 +325,7 @@ tp_status_t run(const LinearDesc& d, hipStream_t stream) {
         P = std::min<int64_t>(G * C, (int64_t)device_cus());
     } else {
         const int64_t target = TP_SKINNY_WG_PER_CU * (int64_t)device_cus();
-        int64_t S = ceil_div(target, G);
+        int64_t S = whole_k ? 1 : ceil_div(target, G);
         const int64_t smax = std::max<int64_t>(1, d.K / (NW * KS));
         S = std::min<int64_t>(std::max<int64_t>(S, 1), std::min<int64_t>(smax, 64));
         CK = ceil_div(ceil_div(d.K, S), KS) * KS;
@@ -344,13 +351,13 @@ tp_status_t run(const LinearDesc& d, hipStream_t stream) {
 }
 
 template <int MT, int RT, int NW, int U, bool PERSIST, int ACT>
-tp_status_t run_bias(const LinearDesc& d, hipStream_t stream) {
+tp_status_t run_bias(const LinearDesc& d, hipStream_t stream, bool whole_k = false) {
     const bool bias = d.b0 != nullptr;
     if (d.out_dtype == TP_DTYPE_BF16)
-        return bias ? run<MT, RT, NW, U, PERSIST, ACT, true, bf16>(d, stream)
-                    : run<MT, RT, NW, U, PERSIST, ACT, false, bf16>(d, stream);
-    return bias ? run<MT, RT, NW, U, PERSIST, ACT, true, float>(d, stream)
-                : run<MT, RT, NW, U, PERSIST, ACT, false, float>(d, stream);
+        return bias ? run<MT, RT, NW, U, PERSIST, ACT, true, bf16>(d, stream, whole_k)
+                    : run<MT, RT, NW, U, PERSIST, ACT, false, bf16>(d, stream, whole_k);
+    return bias ? run<MT, RT, NW, U, PERSIST, ACT, true, float>(d, stream, whole_k)
+                : run<MT, RT, NW, U, PERSIST, ACT, false, float>(d, stream, whole_k);
 }
 
 }  // namespace
@@ -359,7 +366,15 @@ tp_status_t launch_skinny(const LinearDesc& d, hipStream_t stream) {
     const int mt = (int)ceil_div(d.M, 16);
     if (d.swiglu) {
         switch (mt) {
-            case 1: return run_bias<1, 2, 8, TP_SKINNY_U1, false, kActSwiglu>(d, stream);
+            case 1:
+                // From TP_SKINNY_M4G tokens on, two gate and two up tiles per wave halve the token
+                // reloads, which then cost more than the shorter weight stream per wave. Only
+                // where those 32-output row groups by themselves occupy at least 80% of the CUs:
+                // K is then not split, as the cross-workgroup reduction of a split costs more
+                // than the reloads saved (measured on the 70B and 7B FFN shards).
+                if (d.M >= TP_SKINNY_M4G && ceil_div(d.N, 32) * 5 >= (int64_t)device_cus() * 4)
+                    return run_bias<1, 4, 8, 2, false, kActSwiglu>(d, stream, true);
+                return run_bias<1, 2, 8, TP_SKINNY_U1, false, kActSwiglu>(d, stream);
             case 2: return run_bias<2, 2, 4, 2, false, kActSwiglu>(d, stream);
             case 3: return run_bias<3, 2, 4, 2, false, kActSwiglu>(d, stream);
             case 4: return run_bias<4, 4, 4, TP_SKINNY_U4, true, kActSwiglu>(d, stream);
@@ -369,7 +384,11 @@ tp_status_t launch_skinny(const LinearDesc& d, hipStream_t stream) {
     auto plain = [&](auto act) -> tp_status_t {
         constexpr int A = decltype(act)::value;
         switch (mt) {
-            case 1: return run_bias<1, 1, 8, TP_SKINNY_U1, false, A>(d, stream);
+            case 1:
+                // From TP_SKINNY_M2 tokens on, two row tiles per token load halve the token
+                // reloads (measured: 70B TP=4 down at 16 tokens 34 -> 26 us).
+                if (d.M >= TP_SKINNY_M2) return run_bias<1, 2, 8, 2, false, A>(d, stream);
+                return run_bias<1, 1, 8, TP_SKINNY_U1, false, A>(d, stream);
             case 2: return run_bias<2, 2, 4, 2, false, A>(d, stream);
             case 3: return run_bias<3, 2, 4, 2, false, A>(d, stream);
             case 4: return run_bias<4, 4, 4, TP_SKINNY_U4, true, A>(d, stream);

@@ -179,6 +179,47 @@ def test_mlp_shard_fp32_and_skip_down():
     assert err(H_r, ref) <= F32_TOL
 
 
+# ---- decode tile choices: SwiGLU pair with two gate + two up tiles per wave and whole K (from 3
+# tokens, where the 32-output row groups fill the chip), plain products with two row tiles (from 5
+# tokens); ragged output counts, K tails, bias, bitwise reproducibility; M=2 stays on the default.
+
+@pytest.mark.parametrize("M,K,I_,bias", [(3, 1000, 6600, True), (9, 4096, 7168, False),
+                                         (16, 8192, 7176, True), (2, 1000, 6600, False)])
+def test_decode_swiglu_wide_tiles(M, K, I_, bias):
+    log_case("decode swiglu wide tiles", M, K, I_, bias)
+    wg, wu = I.weight(I_, K, 60 + M), I.weight(I_, K, 61 + M)
+    bg, bu = (I.bias(I_, 62), I.bias(I_, 63)) if bias else (None, None)
+    x = I.activations(M, K, 64 + M)
+    X, Wg, Wu, Bg, Bu = dev(x), dev(wg), dev(wu), dev(bg), dev(bu)
+    buf, H = canary_buffer((M, I_), torch.bfloat16)
+    tp.tp_mlp_shard(X, Wg, Wu, Bg, Bu, None, H, None, M, K, I_, 1)
+    H2 = torch.empty(M, I_, dtype=torch.bfloat16, device="cuda")
+    tp.tp_mlp_shard(X, Wg, Wu, Bg, Bu, None, H2, None, M, K, I_, 1)
+    torch.cuda.synchronize()
+    ref = O.swiglu(O.linear(host64(x), host64(wg), None if bg is None else host64(bg)),
+                   O.linear(host64(x), host64(wu), None if bu is None else host64(bu)))
+    assert err(H, ref) <= BF16_TOL
+    assert canaries_intact(buf, (M, I_))
+    assert torch.equal(H, H2)
+
+
+@pytest.mark.parametrize("M,K,N,bias", [(5, 1000, 8200, True), (12, 7000, 8192, False), (16, 4096, 4104, True),
+                                        (4, 1000, 8200, False)])
+def test_decode_plain_two_tiles(M, K, N, bias):
+    log_case("decode plain two tiles", M, K, N, bias)
+    x, w = I.activations(M, K, 70 + M), I.weight(N, K, 71 + M)
+    b = I.bias(N, 72) if bias else None
+    X, W, B = dev(x), dev(w), dev(b)
+    buf, Y = canary_buffer((M, N), torch.bfloat16)
+    tp.tp_linear_col(X, W, B, Y, M, K, N, 1)
+    Y2 = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    tp.tp_linear_col(X, W, B, Y2, M, K, N, 1)
+    torch.cuda.synchronize()
+    assert err(Y, O.linear(host64(x), host64(w), None if b is None else host64(b))) <= BF16_TOL
+    assert canaries_intact(buf, (M, N))
+    assert torch.equal(Y, Y2)
+
+
 # ---- head-split attention projections ----------------------------------------------------------
 
 @pytest.mark.parametrize("M", [1, 9, 130])
