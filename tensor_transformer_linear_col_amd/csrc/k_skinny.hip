@@ -375,8 +375,13 @@ tp_status_t launch_skinny(const LinearDesc& d, hipStream_t stream) {
                 if (d.M >= TP_SKINNY_M4G && ceil_div(d.N, 32) * 5 >= (int64_t)device_cus() * 4)
                     return run_bias<1, 4, 8, 2, false, kActSwiglu>(d, stream, true);
                 return run_bias<1, 2, 8, TP_SKINNY_U1, false, kActSwiglu>(d, stream);
-            case 2: return run_bias<2, 2, 4, 2, false, kActSwiglu>(d, stream);
-            case 3: return run_bias<3, 2, 4, 2, false, kActSwiglu>(d, stream);
+            case 2:  // the same choice for two token tiles (measured: 70B TP=4 at 32 tokens 68 -> 61 us)
+                if (ceil_div(d.N, 32) * 5 >= (int64_t)device_cus() * 4)
+                    return run_bias<2, 4, 8, 2, false, kActSwiglu>(d, stream, true);
+                return run_bias<2, 2, 4, 2, false, kActSwiglu>(d, stream);
+            case 3:  // three token tiles run as four: 1 + 1 tiles per wave reload tokens more than the
+                     // padded rows cost (measured: 70B TP=4 at 48 tokens 79 -> 63 us, 7B TP=2 42 -> 35 us)
+                return run_bias<4, 4, 4, TP_SKINNY_U4, true, kActSwiglu>(d, stream);
             case 4: return run_bias<4, 4, 4, TP_SKINNY_U4, true, kActSwiglu>(d, stream);
             default: return TP_ERR_SHAPE;
         }
