@@ -374,6 +374,12 @@ tp_status_t launch_skinny(const LinearDesc& d, hipStream_t stream) {
                 // than the reloads saved (measured on the 70B and 7B FFN shards).
                 if (d.M >= TP_SKINNY_M4G && ceil_div(d.N, 32) * 5 >= (int64_t)device_cus() * 4)
                     return run_bias<1, 4, 8, 2, false, kActSwiglu>(d, stream, true);
+                // A long weight stream (>= 640 KB per CU) is dealt in equal ranges, one workgroup
+                // per CU: one workgroup per row group leaves some CUs two row groups and others
+                // one (measured: 70B TP=4 at 1 token 51.4 -> 48 us; the 7B TP=2 shard, 352 KB per
+                // CU, is faster with one workgroup per row group).
+                if (4 * d.N * d.K >= (int64_t)device_cus() * (640 << 10))
+                    return run_bias<1, 2, 8, TP_SKINNY_U1, true, kActSwiglu>(d, stream);
                 return run_bias<1, 2, 8, TP_SKINNY_U1, false, kActSwiglu>(d, stream);
             case 2:  // the same choice for two token tiles (measured: 70B TP=4 at 32 tokens 68 -> 61 us)
                 if (ceil_div(d.N, 32) * 5 >= (int64_t)device_cus() * 4)
