@@ -250,18 +250,34 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(SkinnyParams p) {
                     const int ln = q & 63;
                     const int tj = q >> 6;
                     const int j = tj % MT, t = tj / MT;
+                    // NB contributors' loads in flight at a time (clamped indices past the
+                    // last are loaded and not added), summed in workgroup order.
+                    constexpr int NB = MT * RT >= 8 ? 1 : (SWIGLU ? 2 : 4);  // register budget
                     float gv[4] = {0.f, 0.f, 0.f, 0.f}, uv[4] = {0.f, 0.f, 0.f, 0.f};
-                    for (int64_t ow = wfirst; ow <= wlast; ++ow) {
-                        const bool first = !PERSIST || range_begin(ow, p.U, p.P) / p.C == g;
-                        const float* src = p.ws + (ow * 2 + (first ? 0 : 1)) * TILEF;
+                    for (int64_t ob = wfirst; ob <= wlast; ob += NB) {
+                        float xg[NB][4], xu[NB][4];
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            gv[e] += __hip_atomic_load(src + ((t * MT + j) * 4 + e) * 64 + ln, __ATOMIC_RELAXED,
-                                                       __HIP_MEMORY_SCOPE_AGENT);
-                            if (SWIGLU)
-                                uv[e] += __hip_atomic_load(src + (((t + RH) * MT + j) * 4 + e) * 64 + ln,
-                                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        for (int b = 0; b < NB; ++b) {
+                            const int64_t ow = min(ob + b, wlast);
+                            const bool first = !PERSIST || range_begin(ow, p.U, p.P) / p.C == g;
+                            const float* src = p.ws + (ow * 2 + (first ? 0 : 1)) * TILEF;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                xg[b][e] = __hip_atomic_load(src + ((t * MT + j) * 4 + e) * 64 + ln, __ATOMIC_RELAXED,
+                                                             __HIP_MEMORY_SCOPE_AGENT);
+                                xu[b][e] = SWIGLU ? __hip_atomic_load(src + (((t + RH) * MT + j) * 4 + e) * 64 + ln,
+                                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                                  : 0.f;
+                            }
                         }
+#pragma unroll
+                        for (int b = 0; b < NB; ++b)
+                            if (ob + b <= wlast)
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) {
+                                    gv[e] += xg[b][e];
+                                    uv[e] += xu[b][e];
+                                }
                     }
                     epilogue4<ACT, BIAS, OutT>(p.o, g * 16 * RH + t * 16 + 4 * (ln >> 4), j * 16 + (ln & 15), gv,
                                                   uv);

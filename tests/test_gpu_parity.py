@@ -85,7 +85,8 @@ def test_linear_col_bf16(M, K, N, bias):
     assert canaries_intact(buf, (M, N))
 
 
-@pytest.mark.parametrize("M,K,N", [(1, 4096, 1280), (37, 2048, 96), (300, 1024, 264)])
+@pytest.mark.parametrize("M,K,N", [(1, 4096, 1280), (9, 4096, 1280), (16, 1000, 8200), (37, 2048, 96),
+                                   (64, 2056, 520), (300, 1024, 264)])
 def test_linear_col_bf16_fp32_partial_out(M, K, N):
     """bf16 inputs with fp32 outputs (the row layer's fp32-partial option) are tighter."""
     log_case("row partial fp32 out", M, K, N)
