@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="run only the decode sections and print their JSON (for a kernel trace)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time")
     ap.add_argument("--traffic-copy-mib", type=int, default=0,
                     help="first run one plain contiguous copy of this many MiB (counter calibration)")
@@ -474,6 +476,9 @@ def main():
     import torch
     import tp_inputs as I
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.decode_only:
+        print(json.dumps({"decode": decode_bench(), "attention_decode": attention_decode_bench()}), flush=True)
+        return
     if args.traffic_copy_mib > 0:
         # A plain copy of known size: reads and writes exactly n bytes each. Under
         # rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE it calibrates the counters.
