@@ -12,6 +12,8 @@
 //   copy2d: a strided block copy (taking a weight shard).
 #include <algorithm>
 
+#include <type_traits>
+
 #include "tp_internal.h"
 
 namespace tp {
@@ -62,18 +64,30 @@ __device__ __forceinline__ void store8<float>(float* dst, const float v[8]) {
     *reinterpret_cast<floatx4*>(dst + 4) = floatx4{v[4], v[5], v[6], v[7]};
 }
 
-template <typename PT, typename OT, bool BIAS>
+// PC: the number of partials when known at compile time (their loads are then all issued
+// before the first add, instead of one HBM round trip per partial), else 0.
+template <typename PT, typename OT, bool BIAS, int PC>
 __global__ __launch_bounds__(256) void combine_sum_kernel(PtrPack pk, int P, const OT* b, OT* Y, int64_t total,
                                                           int64_t N, int vec) {
     const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
     if (i0 >= total) return;
     if (vec && i0 + 8 <= total) {
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int r = 0; r < P; ++r) {
-            float v[8];
-            load8<PT>(static_cast<const PT*>(pk.p[r]) + i0, v);
+        if constexpr (PC > 0) {
+            float v[PC][8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] += v[e];
+            for (int r = 0; r < PC; ++r) load8<PT>(static_cast<const PT*>(pk.p[r]) + i0, v[r]);
+#pragma unroll
+            for (int r = 0; r < PC; ++r)  // rank order
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] += v[r][e];
+        } else {
+            for (int r = 0; r < P; ++r) {
+                float v[8];
+                load8<PT>(static_cast<const PT*>(pk.p[r]) + i0, v);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] += v[e];
+            }
         }
         if (BIAS) {
             int64_t n = i0 % N;
@@ -152,12 +166,21 @@ tp_status_t sum_typed(const PtrPack& pk, int p, const void* b, void* Y, int64_t 
                       hipStream_t stream) {
     const int64_t total = M * N;
     const unsigned grid = (unsigned)ceil_div(ceil_div(total, 8), 256);
-    if (b)
-        hipLaunchKernelGGL((combine_sum_kernel<PT, OT, true>), dim3(grid), dim3(256), 0, stream, pk, p,
-                           static_cast<const OT*>(b), static_cast<OT*>(Y), total, N, vec);
-    else
-        hipLaunchKernelGGL((combine_sum_kernel<PT, OT, false>), dim3(grid), dim3(256), 0, stream, pk, p,
-                           static_cast<const OT*>(nullptr), static_cast<OT*>(Y), total, N, vec);
+    auto go = [&](auto pc) {
+        constexpr int PC = decltype(pc)::value;
+        if (b)
+            hipLaunchKernelGGL((combine_sum_kernel<PT, OT, true, PC>), dim3(grid), dim3(256), 0, stream, pk, p,
+                               static_cast<const OT*>(b), static_cast<OT*>(Y), total, N, vec);
+        else
+            hipLaunchKernelGGL((combine_sum_kernel<PT, OT, false, PC>), dim3(grid), dim3(256), 0, stream, pk, p,
+                               static_cast<const OT*>(nullptr), static_cast<OT*>(Y), total, N, vec);
+    };
+    switch (p) {
+        case 2: go(std::integral_constant<int, 2>{}); break;
+        case 4: go(std::integral_constant<int, 4>{}); break;
+        case 8: go(std::integral_constant<int, 8>{}); break;
+        default: go(std::integral_constant<int, 0>{}); break;
+    }
     return hip_status();
 }
 
