@@ -183,13 +183,15 @@ def test_mlp_shard_fp32_and_skip_down():
 # ---- decode tile choices: SwiGLU pair with two gate + two up tiles per wave and whole K (3-32
 # tokens, where the 32-output row groups fill the chip), three token tiles run as four (33-48
 # tokens), plain products with two row tiles (from 5 tokens), equal ranges per CU for long SwiGLU
-# weight streams at 1-2 tokens; ragged output counts, K tails, bias, bitwise reproducibility.
+# weight streams (1-2 tokens, or more where the 2 + 2 row groups do not fill the chip); ragged
+# output counts, K tails, bias, bitwise reproducibility.
 
 @pytest.mark.parametrize("M,K,I_,bias", [(3, 1000, 6600, True), (9, 4096, 7168, False),
                                          (16, 8192, 7176, True), (2, 1000, 6600, False),
                                          (20, 2056, 6600, True), (32, 4096, 7176, False),
                                          (40, 1000, 6600, True), (48, 2048, 1000, False),
-                                         (1, 8192, 7176, True), (2, 6000, 7000, False)])
+                                         (1, 8192, 7176, True), (2, 6000, 7000, False),
+                                         (12, 16384, 4104, True)])
 def test_decode_swiglu_wide_tiles(M, K, I_, bias):
     log_case("decode swiglu wide tiles", M, K, I_, bias)
     wg, wu = I.weight(I_, K, 60 + M), I.weight(I_, K, 61 + M)
