@@ -16,8 +16,9 @@
 //   * hands out the work as the list of (row group, K chunk) units, row group major,
 //     cut into one contiguous range per workgroup. With one unit per workgroup this
 //     is a plain split-K grid; with one workgroup per CU and equal ranges (used for
-//     the largest token tiles, whose register footprint allows one workgroup per CU)
-//     every CU streams the same number of bytes whatever the shard's shape.
+//     the 33-64 token tiles, whose register footprint allows one workgroup per CU, and
+//     for long SwiGLU weight streams) every CU streams the same number of bytes
+//     whatever the shard's shape.
 // Every reduction has a fixed order, so results are bitwise reproducible.
 //
 // MFMA 16x16x32 operand mapping used here (lane l, l16 = l % 16, lg = l / 16):
