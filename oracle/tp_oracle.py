@@ -42,8 +42,10 @@ Parity status per function (what pins it, beside itself):
       normal CDF values); the FFN by the sharded-equals-unsharded invariant.
   qkv head layout / attention stand-in (A := Q):  parity unpinned by the
       pages (self-consistency invariants only).
-  kv_heads_of with more shards than KV heads (replication):  a reading,
-      parity unpinned by the pages (self-consistency invariants only).
+  kv_heads_of / qkv_segments / qkv_unreplicate with more shards than KV heads
+      (replication):  a reading, parity unpinned by the pages (self-consistency
+      invariants only: every replica's K/V segment equals its head's columns of the
+      unsharded QKV, and the de-replicated concat equals the unsharded QKV).
   blocks_of / row_shard_uneven:  pinned by the uneven-split invariant of [P5]
       "Try it yourself" and brute force.
   attention_core_shard:  the core is not on the pages (a reading: causal,
@@ -344,8 +346,30 @@ def qkv_shard(wqkv, bqkv, n_heads, n_kv_heads, head_dim, p, r):
 
 
 def qkv_segments(n_heads, n_kv_heads, head_dim, p):
-    """Per-shard segment widths of the fused output: (Q, K, V)."""
-    return (n_heads // p * head_dim, n_kv_heads // p * head_dim, n_kv_heads // p * head_dim)
+    """Per-shard segment widths of the fused output: (Q, K, V) = (Hq/p heads, the shard's KV
+    heads, the shard's KV heads), each head head_dim wide. A shard holds G/p KV heads when p
+    divides G, and the one replicated KV head when p is a multiple of G (kv_heads_of)."""
+    if n_heads % p:
+        raise ValueError("tensor_parallel_size must divide the head counts")
+    hk = len(kv_heads_of(n_kv_heads, p, 0))
+    return (n_heads // p * head_dim, hk * head_dim, hk * head_dim)
+
+
+def qkv_unreplicate(qkv_cat, n_heads, n_kv_heads, head_dim, p):
+    """The unsharded [Q | K | V] columns from the segment concat of all p shards' QKV outputs.
+
+    When p divides G the concat already is the unsharded layout. When KV heads are
+    replicated (p a multiple of G) the concat's K and V blocks hold p heads, head
+    floor(r*G/p) at block r, so KV head h is taken from its first holder, shard h*p/G.
+    Index selection only."""
+    qkv_cat = f64(qkv_cat)
+    if n_kv_heads % p == 0:
+        return qkv_cat
+    d, nq = head_dim, n_heads * head_dim
+    first = [h * p // n_kv_heads for h in range(n_kv_heads)]
+    k = [qkv_cat[:, nq + r * d:nq + (r + 1) * d] for r in first]
+    v = [qkv_cat[:, nq + (p + r) * d:nq + (p + r + 1) * d] for r in first]
+    return np.concatenate([qkv_cat[:, :nq]] + k + v, axis=-1)
 
 
 def attn_proj_shard(x, wqkv_r, bqkv_r, a_r, wo_r):
@@ -441,7 +465,7 @@ def layer_sharded(x, w, p):
     y1 = combine_sum(o_parts, w.get("bo"))
     mlp_parts = mlp_shards(y1, w["Wg"], w["Wu"], w["Wd"], p, w.get("bg"), w.get("bu"))
     y = combine_sum([pr for _, pr in mlp_parts], w.get("bd"))
-    qkv = concat(qkv_parts, qkv_segments(nh, nkv, d, p))
+    qkv = qkv_unreplicate(concat(qkv_parts, qkv_segments(nh, nkv, d, p)), nh, nkv, d, p)
     h = concat([h_r for h_r, _ in mlp_parts])
     return {"qkv": qkv, "y1": y1, "h": h, "y": y}
 

@@ -94,6 +94,20 @@ def _kv_heads_of_no_replication(n_kv_heads, p, r):
     return [r % n_kv_heads]          # round-robin instead of consecutive blocks
 
 
+def _qkv_segments_floor(n_heads, n_kv_heads, head_dim, p):
+    return (n_heads // p * head_dim, n_kv_heads // p * head_dim, n_kv_heads // p * head_dim)
+
+
+def _qkv_unreplicate_ignores_replicas(qkv_cat, n_heads, n_kv_heads, head_dim, p):
+    """Takes the first G K/V blocks of the concat as if no head were replicated."""
+    qkv_cat = T.f64(qkv_cat)
+    d, nq = head_dim, n_heads * head_dim
+    blocks = p if n_kv_heads % p else n_kv_heads
+    k = qkv_cat[:, nq:nq + n_kv_heads * d]
+    v = qkv_cat[:, nq + blocks * d:nq + (blocks + n_kv_heads) * d]
+    return np.concatenate([qkv_cat[:, :nq], k, v], axis=-1)
+
+
 def _kv_group_round_robin(h, hq, hk):
     return h % hk
 
@@ -169,6 +183,8 @@ MUTATIONS = [
     ("attention_core_shard", _attention_unscaled, [P.test_attention_tiny_by_bruteforce]),
     ("attention_core_shard", _attention_no_mask, [P.test_attention_uniform_scores_give_prefix_means,
                                                   P.test_attention_first_causal_row_and_dominant_key]),
+    ("qkv_segments", _qkv_segments_floor, [P.test_qkv_segments_and_concat_with_replicated_kv_heads]),
+    ("qkv_unreplicate", _qkv_unreplicate_ignores_replicas, [P.test_qkv_segments_and_concat_with_replicated_kv_heads]),
     ("kv_heads_of", _kv_heads_of_no_replication, [P.test_kv_heads_replicated_when_more_shards_than_kv_heads]),
     ("attention_decode_shard", _decode_excludes_self, [P.test_attention_decode_over_cache_equals_the_full_causal_pass,
                                                        P.test_attention_decode_single_token_by_bruteforce]),

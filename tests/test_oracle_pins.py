@@ -236,6 +236,45 @@ def test_kv_heads_replicated_when_more_shards_than_kv_heads():
         np.testing.assert_array_equal(y[:, (hq + 1) * d:], full[:, (nh + nkv + h) * d:(nh + nkv + h + 1) * d])
 
 
+def test_qkv_segments_and_concat_with_replicated_kv_heads():
+    """Replication (a reading, parity unpinned by the pages): with p a multiple of G each shard's
+    K and V segments are one head wide; every replica's K/V segment equals that KV head's
+    columns of the unsharded QKV, and the segment concat with each head taken from its first
+    holder is the unsharded QKV. The sharded layer chain then matches the unsharded one."""
+    assert O.qkv_segments(64, 8, 128, 16) == (512, 128, 128)
+    assert O.qkv_segments(64, 8, 128, 8) == (1024, 128, 128)
+    assert O.qkv_segments(64, 8, 128, 4) == (2048, 256, 256)
+    assert O.qkv_segments(16, 2, 64, 8) == (128, 64, 64)
+    with pytest.raises(ValueError):
+        O.qkv_segments(64, 8, 128, 12)
+    nh, nkv, d, hid, p = 8, 2, 4, 16, 8
+    shape = I.LayerShape("t", hidden=hid, n_heads=nh, n_kv_heads=nkv, head_dim=d, tp=p, seed=13)
+    wt = {k: I.as_numpy_f64(v) for k, v in I.attn_weights(shape).items()}
+    x = I.as_numpy_f64(I.activations(3, hid, seed=131))
+    full = O.linear(x, wt["Wqkv"], wt["bqkv"])
+    seg = O.qkv_segments(nh, nkv, d, p)
+    parts = [O.col_linear(x, *O.qkv_shard(wt["Wqkv"], wt["bqkv"], nh, nkv, d, p, r)) for r in range(p)]
+    for r, y in enumerate(parts):
+        assert y.shape[1] == sum(seg)
+        h = r * nkv // p
+        np.testing.assert_array_equal(y[:, seg[0]:seg[0] + seg[1]], full[:, (nh + h) * d:(nh + h + 1) * d])
+        np.testing.assert_array_equal(y[:, seg[0] + seg[1]:], full[:, (nh + nkv + h) * d:(nh + nkv + h + 1) * d])
+    cat = O.concat(parts, seg)
+    assert cat.shape[1] == (nh + 2 * p) * d
+    np.testing.assert_array_equal(O.qkv_unreplicate(cat, nh, nkv, d, p), full)
+    # without replication the concat already is the unsharded layout
+    parts2 = [O.col_linear(x, *O.qkv_shard(wt["Wqkv"], wt["bqkv"], nh, nkv, d, 2, r)) for r in range(2)]
+    np.testing.assert_array_equal(O.qkv_unreplicate(O.concat(parts2, O.qkv_segments(nh, nkv, d, 2)), nh, nkv, d, 2),
+                                  full)
+    # the layer chain over 8 shards with 2 KV heads equals the unsharded chain
+    shape = I.LayerShape("t", hidden=hid, intermediate=24, n_heads=nh, n_kv_heads=nkv, head_dim=d, tp=p, seed=14)
+    w = {k: I.as_numpy_f64(v) for k, v in {**I.attn_weights(shape), **I.ffn_weights(shape)}.items()}
+    w.update(n_heads=nh, n_kv_heads=nkv, head_dim=d)
+    got = O.layer_sharded(x, w, p)
+    np.testing.assert_array_equal(got["qkv"], O.linear(x, w["Wqkv"], w["bqkv"]))
+    assert O.rel_err(got["y"], O.layer_unsharded(x, w)) <= 1e-12
+
+
 def _qkv(m, hq, hk, d, seed):
     return I.as_numpy_f64(I.activations(m, (hq + 2 * hk) * d, seed=seed))
 
