@@ -50,6 +50,18 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def reserve_for(fn):
+    """Size the library's work space for the current stream with a dry run of fn (which
+    validates and plans its calls but enqueues nothing), then reserve it. Setup only: the
+    timed calls themselves never allocate."""
+    import tensor_transformer_linear_col_amd as tp
+    with tp.tp_plan() as need:
+        fn()
+    if need.partial_bytes or need.n_counters:
+        tp.tp_workspace_reserve(need.partial_bytes, need.n_counters)
+    return need
+
+
 # ----------------------------------------------------------------------------------------
 # The layer
 # ----------------------------------------------------------------------------------------
@@ -117,6 +129,8 @@ class Layer:
             "down": 2.0 * M * h * self.i * p,
         }
         self.total_flops = sum(self.flops.values())
+        need = reserve_for(lambda: (self.step(), self.step(core=True)))
+        log(f"work space: {need.partial_bytes / 2**20:.1f} MiB of partials, {need.n_counters} counters")
 
     def step(self, ev=None, core=False, only=None):
         """One pass of the shard path. ev: optional dict name -> list of (start, end) events,
@@ -217,6 +231,7 @@ def attention_decode_bench(reps=50):
         for M in (1, 16):
             Q = torch.randn(M, (hq + 2 * hk) * d, generator=g).to(torch.bfloat16).cuda()
             A = torch.empty(M, hq * d, dtype=torch.bfloat16, device="cuda")
+            reserve_for(lambda: tp.tp_attn_decode_shard(Q, Kc, Vc, T, A, M, nh, nkv, d, p))
             tp.tp_attn_decode_shard(Q, Kc, Vc, T, A, M, nh, nkv, d, p)
             torch.cuda.synchronize()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -274,6 +289,8 @@ def decode_bench(iters=30):
             x = I.activations(M, h, I.activation_seed(shape.seed, M)).cuda()
             H = torch.empty(M, i, dtype=BF, device="cuda")
             P = torch.empty(M, h, dtype=BF, device="cuda")
+            reserve_for(lambda: (tp.tp_mlp_shard(x, *sets[0][:2], None, None, None, H, None, M, h, inter, p),
+                                 tp.tp_linear_row_partial(H, i, sets[0][2], P, M, inter, h, p)))
             for c in range(len(sets)):  # warm
                 Wg, Wu, Wd = sets[c]
                 tp.tp_mlp_shard(x, Wg, Wu, None, None, None, H, None, M, h, inter, p)
@@ -343,6 +360,8 @@ def decode_bench(iters=30):
         x = I.activations(M, h, I.activation_seed(shape.seed, M)).cuda()
         H = torch.empty(M, i, dtype=BF, device="cuda")
         P = torch.empty(M, h, dtype=BF, device="cuda")
+        reserve_for(lambda: (tp.tp_ffn_gelu_shard(x, sets[0][0], sets[0][1], None, H, None, M, h, inter, p),
+                             tp.tp_linear_row_partial(H, i, sets[0][2], P, M, inter, h, p)))
         for c in range(len(sets)):  # warm
             W1, b1, W2 = sets[c]
             tp.tp_ffn_gelu_shard(x, W1, b1, None, H, None, M, h, inter, p)
@@ -408,6 +427,7 @@ def split_variants_bench(iters=30):
     x = I.activations(1, h, seed=902).cuda()
     y = torch.empty(1, width, dtype=BF, device="cuda")
     fn = lambda c: tp.tp_linear_col(x, sets[c], None, y, 1, h, width, 1)
+    reserve_for(lambda: fn(0))
     for c in range(len(sets)):
         fn(c)
     torch.cuda.synchronize()
@@ -426,6 +446,7 @@ def split_variants_bench(iters=30):
     x = I.activations(1, hid, seed=904).cuda()
     q = torch.empty(1, nq, dtype=BF, device="cuda")
     fn = lambda c: tp.tp_attn_proj_shard(x, sets[c], None, q, None, None, None, 1, hid, nh, nkv, d, p)
+    reserve_for(lambda: fn(0))
     for c in range(len(sets)):
         fn(c)
     torch.cuda.synchronize()

@@ -33,11 +33,19 @@
  *   - Alignment: every base pointer and every row stride in bytes must be a
  *     multiple of 16 (TP_ERR_ALIGN otherwise). For bf16 this means K % 8 == 0,
  *     for fp32 K % 4 == 0, for every row length that is read or written.
- *   - Work space: kernels that split the reduction dimension across workgroups
- *     keep fp32 partial sums in a device work space owned by the library, one per
- *     (device, stream), allocated with hipMalloc on the first call that needs it
- *     and grown when a larger one is needed. Calls on the same stream are
- *     ordered by the stream; tp_release_workspaces() frees them all.
+ *   - Work space: kernels that split a reduction across workgroups keep fp32
+ *     partial sums and arrival counters in a device work space, one per (device,
+ *     stream), which the caller reserves once at setup with tp_workspace_reserve
+ *     (the only call that allocates; it may synchronise the stream when it
+ *     replaces a smaller space). A dry run between tp_plan_begin and tp_plan_end
+ *     reports the size a sequence of calls needs. The compute calls never
+ *     allocate, free or synchronise: a call whose launches need more work space
+ *     than is reserved for its device and stream returns TP_ERR_WORKSPACE having
+ *     enqueued nothing. Calls that split no reduction need no reservation. Calls
+ *     on one stream are ordered by the stream and share its space; calls on
+ *     different streams use different spaces. tp_release_workspaces() frees them.
+ *   - Every call checks all of its launches (including their work space) before it
+ *     enqueues the first one, so any error leaves the stream untouched.
  *   - Results are deterministic: every reduction runs in a fixed order.
  *   - Errors are returned, never raised; TP_ERR_HIP reports a failed launch or
  *     allocation (hipGetLastError after the launch).
@@ -45,6 +53,7 @@
 #ifndef TP_LINEAR_H
 #define TP_LINEAR_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -64,11 +73,13 @@ typedef enum {
     TP_ERR_INDIVISIBLE = 3, /* a size that is split by tp_size is not divisible by it */
     TP_ERR_DTYPE = 4,       /* unknown dtype, or an fp32 input with bf16 partials */
     TP_ERR_ALIGN = 5,       /* a pointer or row stride is not a multiple of 16 bytes */
-    TP_ERR_HIP = 6          /* the HIP runtime reported an error */
+    TP_ERR_HIP = 6,         /* the HIP runtime reported an error */
+    TP_ERR_WORKSPACE = 7    /* the reserved work space of this device and stream is too small */
 } tp_status_t;
 
 /* Column-parallel linear, shard r ([P3] "How ... Under the Hood", column parallelism;
- * [P3] ColumnParallelLinear.forward; [P5] out_gpu0 = x @ W_gpu0.T + b_gpu0).
+ * [P3] ColumnParallelLinear.forward; [P5] simulation script: each GPU's output is its
+ * own weight rows applied to the full input, plus its bias slice).
  *   Y_r[M, out_features/p] = X[M, in_features] * W_r^T + b_r
  *   X   : [M, in_features], the full input, replicated on every shard.
  *   W_r : [out_features/p, in_features], the shard's contiguous block of output rows.
@@ -204,13 +215,6 @@ tp_status_t tp_shard_weight(const void* W, int64_t out_features, int64_t in_feat
                             int32_t tp_size, int32_t rank, int32_t axis, void* W_r,
                             tp_dtype_t dtype, void* stream);
 
-/* Take shard `rank` of a fused [Wq; Wk; Wv] weight ([(Hq + 2G)*d, in_features]) or, with
- * in_features = 1, of its bias: the rows of Q heads r*Hq/p.., K heads r*G/p.., V heads
- * r*G/p.., in that order -> [(Hq/p + 2G/p)*d, in_features]. With more shards than KV heads
- * (tp_size a multiple of G) each KV head is replicated on p/G consecutive shards: shard r
- * holds KV head floor(r*G/p) and its shard is [(Hq/p + 2)*d, in_features]; the same rule
- * holds for tp_attn_proj_shard. TP_ERR_INDIVISIBLE if p does not divide Hq, or neither
- * divides G nor is a multiple of it. */
 /* An uneven split ([P5] "Try it yourself": 9 outputs split 5 + 4 still match exactly): take
  * the block [start, start + width) of W along axis 0 (output rows -> [width, in]) or axis 1
  * (input columns -> [out, width]) into a contiguous buffer. The linear entry points then run
@@ -226,11 +230,38 @@ tp_status_t tp_shard_weight_block(const void* W, int64_t out_features, int64_t i
 tp_status_t tp_combine_concat_v(const void* const* shards, int32_t n_shards, const int64_t* widths,
                                 void* Y, int64_t M, tp_dtype_t dtype, void* stream);
 
+/* Take shard `rank` of a fused [Wq; Wk; Wv] weight ([(Hq + 2G)*d, in_features]) or, with
+ * in_features = 1, of its bias ([P4] "How a layer is split": heads go to different GPUs):
+ * the rows of Q heads r*Hq/p.., K heads r*G/p.., V heads r*G/p.., in that order ->
+ * [(Hq/p + 2G/p)*d, in_features]. With more shards than KV heads (tp_size a multiple of G)
+ * each KV head is replicated on p/G consecutive shards: shard r holds KV head floor(r*G/p)
+ * and its shard is [(Hq/p + 2)*d, in_features]; the same rule holds for tp_attn_proj_shard.
+ * TP_ERR_INDIVISIBLE if p does not divide Hq, or neither divides G nor is a multiple of it.
+ * Exact copy. */
 tp_status_t tp_shard_qkv(const void* Wqkv, int64_t in_features, int32_t n_heads, int32_t n_kv_heads,
                          int32_t head_dim, int32_t tp_size, int32_t rank, void* Wqkv_r,
                          tp_dtype_t dtype, void* stream);
 
-/* Frees every work space the library holds. No call may be in flight on any stream. */
+/* Reserves the work space of the current device and `stream` (see the conventions above):
+ * at least partial_bytes of fp32 partial sums and n_counters arrival counters. Allocates
+ * with hipMalloc and zeroes the counters with a kernel on `stream`; keeps a space that is
+ * already large enough; otherwise synchronises `stream`, frees the old space and takes
+ * one covering both sizes. Setup only: not to be called while the stream is captured.
+ * TP_ERR_HIP if the allocation fails. Inside a dry run it does nothing. */
+tp_status_t tp_workspace_reserve(void* stream, size_t partial_bytes, size_t n_counters);
+
+/* Sizes reserved for the current device and `stream` (0, 0 if none). */
+tp_status_t tp_workspace_reserved(void* stream, size_t* partial_bytes, size_t* n_counters);
+
+/* Dry run of this host thread: after tp_plan_begin, every call validates its arguments and
+ * plans its launches as usual but enqueues nothing and needs no work space; tp_plan_end
+ * returns the largest work space any of those calls needs (partial bytes, counters; either
+ * pointer may be NULL) and ends the dry run. */
+tp_status_t tp_plan_begin(void);
+tp_status_t tp_plan_end(size_t* partial_bytes, size_t* n_counters);
+
+/* Frees every work space the library holds (synchronising each space's stream). No call may
+ * be in flight on any stream. */
 tp_status_t tp_release_workspaces(void);
 
 /* Static, human-readable name of a status code. */

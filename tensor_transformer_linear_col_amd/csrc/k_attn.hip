@@ -538,7 +538,7 @@ int device_cu_count() {
 }
 
 template <int D, bool CAUSAL, bool PACK>
-tp_status_t run_attn(AttnParams p, hipStream_t stream) {
+tp_status_t run_attn(AttnParams p, const Ctx& c) {
     constexpr int QB = 32 * kWQ;
     const int gq = p.hq / p.hk;
     const int HM = PACK ? p.hk : p.hq;
@@ -573,12 +573,17 @@ tp_status_t run_attn(AttnParams p, hipStream_t stream) {
         // with PACK 128 rows x (D + 2) floats.
         const int64_t slots = PACK ? pieces : std::max<int64_t>(pieces, 4 * (int64_t)nqb);
         const size_t floats = (size_t)(slots * HM) * (PACK ? QB * (D + 2) : kWQ * 64 * (D / 2 + 2));
-        Workspace ws;
-        const tp_status_t st = get_workspace(stream, floats, (size_t)nqb * HM, &ws);
-        if (st != TP_OK) return st;
-        p.ws = ws.partials;
-        p.counters = ws.counters;
+        const WsNeed need{floats, (size_t)nqb * HM};
+        if (c.planning()) {
+            c.need->merge(need);
+            return TP_OK;
+        }
+        if (!c.ws || !c.ws->covers(need)) return TP_ERR_WORKSPACE;
+        p.ws = c.ws->partials;
+        p.counters = c.ws->counters;
         p.ml_off = (int64_t)pieces * HM * QB * D;
+    } else if (c.planning()) {
+        return TP_OK;
     }
     // Causal prefill: largest ranges first (a cut block's halves are about half as long as
     // an uncut block of the same index, so the plain walk would queue long uncut blocks
@@ -597,26 +602,26 @@ tp_status_t run_attn(AttnParams p, hipStream_t stream) {
         p.nord = (int)v.size();
     }
     hipLaunchKernelGGL((attn_kernel<D, CAUSAL, PACK, kWQ>), dim3((unsigned)(pieces * HM)), dim3(128 * kWQ), 0,
-                       stream, p);
+                       c.stream, p);
     if (PACK && p.L > 0) {
         const tp_status_t st = hip_status();
         if (st != TP_OK) return st;
-        hipLaunchKernelGGL((attn_merge_kernel<D>), dim3((unsigned)(nqb * HM * QB)), dim3(256), 0, stream, p, nqb);
+        hipLaunchKernelGGL((attn_merge_kernel<D>), dim3((unsigned)(nqb * HM * QB)), dim3(256), 0, c.stream, p, nqb);
     }
     return hip_status();
 }
 
 template <bool PACK>
-tp_status_t run_attn_d(const AttnParams& p, int d, bool causal, hipStream_t stream) {
-    if (d == 128) return causal ? run_attn<128, true, PACK>(p, stream) : run_attn<128, false, PACK>(p, stream);
-    if (d == 64) return causal ? run_attn<64, true, PACK>(p, stream) : run_attn<64, false, PACK>(p, stream);
+tp_status_t run_attn_d(const AttnParams& p, int d, bool causal, const Ctx& c) {
+    if (d == 128) return causal ? run_attn<128, true, PACK>(p, c) : run_attn<128, false, PACK>(p, c);
+    if (d == 64) return causal ? run_attn<64, true, PACK>(p, c) : run_attn<64, false, PACK>(p, c);
     return TP_ERR_SHAPE;
 }
 
 }  // namespace
 
 tp_status_t launch_attn_core(const void* qkv, int64_t ldq, void* out, int64_t lda, int64_t M, int hq, int hk, int d,
-                             bool causal, hipStream_t stream) {
+                             bool causal, const Ctx& c) {
     // Buffer offsets are 32-bit: the K and V column blocks must lie within 2 GiB.
     if (M * ldq * 2 >= (int64_t(1) << 31)) return TP_ERR_SHAPE;
     AttnParams p;
@@ -632,20 +637,22 @@ tp_status_t launch_attn_core(const void* qkv, int64_t ldq, void* out, int64_t ld
     p.hq = hq;
     p.hk = hk;
     p.scale_log2 = 1.4426950408889634f / sqrtf((float)d);
-    return run_attn_d<false>(p, d, causal, stream);
+    return run_attn_d<false>(p, d, causal, c);
 }
 
 tp_status_t launch_attn_decode(const void* qkv, int64_t ldq, void* kc, void* vc, int64_t ldkv, int64_t cache_len,
-                               void* out, int64_t lda, int64_t M, int hq, int hk, int d, hipStream_t stream) {
+                               void* out, int64_t lda, int64_t M, int hq, int hk, int d, const Ctx& c) {
     const int64_t n_keys = cache_len + M;
     if (n_keys * ldkv * 2 >= (int64_t(1) << 31)) return TP_ERR_SHAPE;
-    const int64_t units = 2 * M * (ldkv / 8);
-    const unsigned grid = (unsigned)std::min<int64_t>((units + 255) / 256, 4096);
-    hipLaunchKernelGGL(append_kv_kernel, dim3(grid), dim3(256), 0, stream, static_cast<const bf16*>(qkv), ldq,
-                       (int64_t)hq * d, (int64_t)(hq + hk) * d, static_cast<bf16*>(kc), static_cast<bf16*>(vc), ldkv,
-                       cache_len, M);
-    const tp_status_t st = hip_status();
-    if (st != TP_OK) return st;
+    if (!c.planning()) {  // (the plan below covers the attention launches)
+        const int64_t units = 2 * M * (ldkv / 8);
+        const unsigned grid = (unsigned)std::min<int64_t>((units + 255) / 256, 4096);
+        hipLaunchKernelGGL(append_kv_kernel, dim3(grid), dim3(256), 0, c.stream, static_cast<const bf16*>(qkv), ldq,
+                           (int64_t)hq * d, (int64_t)(hq + hk) * d, static_cast<bf16*>(kc), static_cast<bf16*>(vc),
+                           ldkv, cache_len, M);
+        const tp_status_t st = hip_status();
+        if (st != TP_OK) return st;
+    }
     AttnParams p;
     p.q = static_cast<const bf16*>(qkv);
     p.k = static_cast<const bf16*>(kc);
@@ -660,7 +667,7 @@ tp_status_t launch_attn_decode(const void* qkv, int64_t ldq, void* kc, void* vc,
     p.hq = hq;
     p.hk = hk;
     p.scale_log2 = 1.4426950408889634f / sqrtf((float)d);
-    return run_attn_d<true>(p, d, true, stream);
+    return run_attn_d<true>(p, d, true, c);
 }
 
 }  // namespace tp

@@ -90,7 +90,9 @@ __global__ __launch_bounds__(256) void f32_kernel(F32Params p) {
 
 }  // namespace
 
-tp_status_t launch_f32(const LinearDesc& d, hipStream_t stream) {
+tp_status_t launch_f32(const LinearDesc& d, const Ctx& c) {
+    if (c.planning()) return TP_OK;  // no work space
+    const hipStream_t stream = c.stream;
     F32Params p;
     p.X = static_cast<const float*>(d.X);
     p.ldx = d.ldx;

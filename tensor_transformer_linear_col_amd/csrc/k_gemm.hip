@@ -644,7 +644,7 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void splitk_reduce_kernel(Ge
 }
 
 template <int TN, int TM, int WAVES_N, int WAVES_M, int ACT, bool BIAS, typename OutT>
-tp_status_t run_dtl(const LinearDesc& d, int cus, hipStream_t stream) {
+tp_status_t run_dtl(const LinearDesc& d, int cus, const Ctx& c) {
     GemmParams p;
     p.X = static_cast<const bf16*>(d.X);
     p.ldx = d.ldx;
@@ -685,39 +685,45 @@ tp_status_t run_dtl(const LinearDesc& d, int cus, hipStream_t stream) {
         }
     }
     if (S == 1) {
+        if (c.planning()) return TP_OK;
         hipLaunchKernelGGL((gemm_dtl_kernel<TN, TM, WAVES_N, WAVES_M, ACT, BIAS, false, OutT>), dim3((unsigned)tiles),
-                           dim3(NT), 0, stream, p);
+                           dim3(NT), 0, c.stream, p);
         return hip_status();
     }
     constexpr int64_t TILEF = (int64_t)TN * (ACT == kActSwiglu ? 2 : 1) * TM;  // floats of a partial tile
+    const WsNeed need{(size_t)(R * S * TILEF), 0};
+    if (c.planning()) {
+        c.need->merge(need);
+        return TP_OK;
+    }
+    if (!c.ws || !c.ws->covers(need)) return TP_ERR_WORKSPACE;
     p.F = (int)F;
     p.S = S;
-    Workspace ws;
-    tp_status_t st = get_workspace(stream, (size_t)(R * S * TILEF), 0, &ws);
-    if (st != TP_OK) return st;
-    p.ws = ws.partials;
+    p.ws = c.ws->partials;
     hipLaunchKernelGGL((gemm_dtl_kernel<TN, TM, WAVES_N, WAVES_M, ACT, BIAS, true, OutT>),
-                       dim3((unsigned)(F + R * S)), dim3(NT), 0, stream, p);
-    st = hip_status();
+                       dim3((unsigned)(F + R * S)), dim3(NT), 0, c.stream, p);
+    const tp_status_t st = hip_status();
     if (st != TP_OK) return st;
     constexpr int BN = TN / WAVES_N / 32;
     hipLaunchKernelGGL((splitk_reduce_kernel<TN, TM, WAVES_N, WAVES_M, ACT, BIAS, OutT>), dim3((unsigned)(R * BN)),
-                       dim3(NT), 0, stream, p);
+                       dim3(NT), 0, c.stream, p);
     return hip_status();
 }
 
 template <int TN, int TM, int WAVES_N, int WAVES_M, int ACT>
-tp_status_t run_dtl_bias(const LinearDesc& d, int cus, hipStream_t stream) {
+tp_status_t run_dtl_bias(const LinearDesc& d, int cus, const Ctx& c) {
     const bool bias = d.b0 != nullptr;
     if (d.out_dtype == TP_DTYPE_BF16)
-        return bias ? run_dtl<TN, TM, WAVES_N, WAVES_M, ACT, true, bf16>(d, cus, stream)
-                    : run_dtl<TN, TM, WAVES_N, WAVES_M, ACT, false, bf16>(d, cus, stream);
-    return bias ? run_dtl<TN, TM, WAVES_N, WAVES_M, ACT, true, float>(d, cus, stream)
-                : run_dtl<TN, TM, WAVES_N, WAVES_M, ACT, false, float>(d, cus, stream);
+        return bias ? run_dtl<TN, TM, WAVES_N, WAVES_M, ACT, true, bf16>(d, cus, c)
+                    : run_dtl<TN, TM, WAVES_N, WAVES_M, ACT, false, bf16>(d, cus, c);
+    return bias ? run_dtl<TN, TM, WAVES_N, WAVES_M, ACT, true, float>(d, cus, c)
+                : run_dtl<TN, TM, WAVES_N, WAVES_M, ACT, false, float>(d, cus, c);
 }
 
 template <int TN, int TM, int WAVES_N, int WAVES_M, int ACT, bool BIAS, bool KTAIL, typename OutT>
-tp_status_t run(const LinearDesc& d, hipStream_t stream) {
+tp_status_t run(const LinearDesc& d, const Ctx& c) {
+    if (c.planning()) return TP_OK;  // no work space
+    const hipStream_t stream = c.stream;
     GemmParams p;
     p.X = static_cast<const bf16*>(d.X);
     p.ldx = d.ldx;
@@ -743,25 +749,25 @@ tp_status_t run(const LinearDesc& d, hipStream_t stream) {
 }
 
 template <int TN, int TM, int WAVES_N, int WAVES_M, int ACT, bool BIAS, bool KTAIL>
-tp_status_t run_out(const LinearDesc& d, hipStream_t stream) {
-    return d.out_dtype == TP_DTYPE_BF16 ? run<TN, TM, WAVES_N, WAVES_M, ACT, BIAS, KTAIL, bf16>(d, stream)
-                                        : run<TN, TM, WAVES_N, WAVES_M, ACT, BIAS, KTAIL, float>(d, stream);
+tp_status_t run_out(const LinearDesc& d, const Ctx& c) {
+    return d.out_dtype == TP_DTYPE_BF16 ? run<TN, TM, WAVES_N, WAVES_M, ACT, BIAS, KTAIL, bf16>(d, c)
+                                        : run<TN, TM, WAVES_N, WAVES_M, ACT, BIAS, KTAIL, float>(d, c);
 }
 
 template <int TN, int TM, int WAVES_N, int WAVES_M, int ACT>
-tp_status_t run_bias(const LinearDesc& d, hipStream_t stream) {
+tp_status_t run_bias(const LinearDesc& d, const Ctx& c) {
     const bool bias = d.b0 != nullptr;
     const bool ktail = d.K % BK != 0;
     if (bias)
-        return ktail ? run_out<TN, TM, WAVES_N, WAVES_M, ACT, true, true>(d, stream)
-                     : run_out<TN, TM, WAVES_N, WAVES_M, ACT, true, false>(d, stream);
-    return ktail ? run_out<TN, TM, WAVES_N, WAVES_M, ACT, false, true>(d, stream)
-                 : run_out<TN, TM, WAVES_N, WAVES_M, ACT, false, false>(d, stream);
+        return ktail ? run_out<TN, TM, WAVES_N, WAVES_M, ACT, true, true>(d, c)
+                     : run_out<TN, TM, WAVES_N, WAVES_M, ACT, true, false>(d, c);
+    return ktail ? run_out<TN, TM, WAVES_N, WAVES_M, ACT, false, true>(d, c)
+                 : run_out<TN, TM, WAVES_N, WAVES_M, ACT, false, false>(d, c);
 }
 
 }  // namespace
 
-tp_status_t launch_gemm(const LinearDesc& d, hipStream_t stream) {
+tp_status_t launch_gemm(const LinearDesc& d, const Ctx& c) {
     // Byte offsets inside an operand are 32-bit.
     if ((int64_t)d.N * d.K * 2 >= (int64_t(1) << 32) || (int64_t)d.M * d.ldx * 2 >= (int64_t(1) << 32))
         return TP_ERR_SHAPE;
@@ -785,17 +791,17 @@ tp_status_t launch_gemm(const LinearDesc& d, hipStream_t stream) {
     if (d.swiglu) {
         const int64_t big = ceil_div(d.N, 128) * ceil_div(d.M, 256);
         if (dma && (big >= cus || big * kt >= 16 * (int64_t)cus))
-            return run_dtl_bias<128, 256, 4, 4, kActSwiglu>(d, cus, stream);
-        if (big >= cus) return run_bias<128, 256, 2, 2, kActSwiglu>(d, stream);
-        return run_bias<64, 128, 2, 2, kActSwiglu>(d, stream);
+            return run_dtl_bias<128, 256, 4, 4, kActSwiglu>(d, cus, c);
+        if (big >= cus) return run_bias<128, 256, 2, 2, kActSwiglu>(d, c);
+        return run_bias<64, 128, 2, 2, kActSwiglu>(d, c);
     }
     const int64_t big = ceil_div(d.N, 256) * ceil_div(d.M, 256);
     auto plain = [&](auto act) -> tp_status_t {
         constexpr int A = decltype(act)::value;
         if (dma && (big >= cus || big * kt >= 16 * (int64_t)cus))
-            return run_dtl_bias<256, 256, 2, 4, A>(d, cus, stream);
-        if (big >= cus) return run_bias<256, 256, 2, 2, A>(d, stream);
-        return run_bias<128, 128, 2, 2, A>(d, stream);
+            return run_dtl_bias<256, 256, 2, 4, A>(d, cus, c);
+        if (big >= cus) return run_bias<256, 256, 2, 2, A>(d, c);
+        return run_bias<128, 128, 2, 2, A>(d, c);
     };
     return d.gelu ? plain(std::integral_constant<int, kActGelu>{}) : plain(std::integral_constant<int, kActNone>{});
 }

@@ -307,7 +307,7 @@ int device_cus() {
 
 // whole_k: never split K across workgroups (one workgroup per row group).
 template <int MT, int RT, int NW, int U, bool PERSIST, int ACT, bool BIAS, typename OutT>
-tp_status_t run(const LinearDesc& d, hipStream_t stream, bool whole_k = false) {
+tp_status_t run(const LinearDesc& d, const Ctx& c, bool whole_k = false) {
     constexpr int RH = ACT == kActSwiglu ? RT / 2 : RT;
     constexpr int KS = 32 * U;
     constexpr int TILEF = RT * MT * 4 * 64;
@@ -355,31 +355,36 @@ tp_status_t run(const LinearDesc& d, hipStream_t stream, bool whole_k = false) {
     p.P = (int)P;
     p.ws = nullptr;
     p.counters = nullptr;
-    if (P != G) {  // some row group is cut
-        Workspace ws;
-        tp_status_t st = get_workspace(stream, (size_t)(P * 2 * TILEF), (size_t)G, &ws);
-        if (st != TP_OK) return st;
-        p.ws = ws.partials;
-        p.counters = ws.counters;
+    if (P != G) {  // some row group is cut: partial tiles and arrival counters
+        const WsNeed need{(size_t)(P * 2 * TILEF), (size_t)G};
+        if (c.planning()) {
+            c.need->merge(need);
+            return TP_OK;
+        }
+        if (!c.ws || !c.ws->covers(need)) return TP_ERR_WORKSPACE;
+        p.ws = c.ws->partials;
+        p.counters = c.ws->counters;
+    } else if (c.planning()) {
+        return TP_OK;
     }
     hipLaunchKernelGGL((skinny_kernel<MT, RT, NW, U, PERSIST, ACT, BIAS, OutT>), dim3((unsigned)P),
-                       dim3(NW * 64), 0, stream, p);
+                       dim3(NW * 64), 0, c.stream, p);
     return hip_status();
 }
 
 template <int MT, int RT, int NW, int U, bool PERSIST, int ACT>
-tp_status_t run_bias(const LinearDesc& d, hipStream_t stream, bool whole_k = false) {
+tp_status_t run_bias(const LinearDesc& d, const Ctx& c, bool whole_k = false) {
     const bool bias = d.b0 != nullptr;
     if (d.out_dtype == TP_DTYPE_BF16)
-        return bias ? run<MT, RT, NW, U, PERSIST, ACT, true, bf16>(d, stream, whole_k)
-                    : run<MT, RT, NW, U, PERSIST, ACT, false, bf16>(d, stream, whole_k);
-    return bias ? run<MT, RT, NW, U, PERSIST, ACT, true, float>(d, stream, whole_k)
-                : run<MT, RT, NW, U, PERSIST, ACT, false, float>(d, stream, whole_k);
+        return bias ? run<MT, RT, NW, U, PERSIST, ACT, true, bf16>(d, c, whole_k)
+                    : run<MT, RT, NW, U, PERSIST, ACT, false, bf16>(d, c, whole_k);
+    return bias ? run<MT, RT, NW, U, PERSIST, ACT, true, float>(d, c, whole_k)
+                : run<MT, RT, NW, U, PERSIST, ACT, false, float>(d, c, whole_k);
 }
 
 }  // namespace
 
-tp_status_t launch_skinny(const LinearDesc& d, hipStream_t stream) {
+tp_status_t launch_skinny(const LinearDesc& d, const Ctx& c) {
     const int mt = (int)ceil_div(d.M, 16);
     if (d.swiglu) {
         switch (mt) {
@@ -390,24 +395,24 @@ tp_status_t launch_skinny(const LinearDesc& d, hipStream_t stream) {
                 // K is then not split, as the cross-workgroup reduction of a split costs more
                 // than the reloads saved (measured on the 70B and 7B FFN shards).
                 if (d.M >= TP_SKINNY_M4G && ceil_div(d.N, 32) * 5 >= (int64_t)device_cus() * 4)
-                    return run_bias<1, 4, 8, 2, false, kActSwiglu>(d, stream, true);
+                    return run_bias<1, 4, 8, 2, false, kActSwiglu>(d, c, true);
                 // A long weight stream (>= 640 KB per CU) is dealt in equal ranges, one workgroup
                 // per CU: one workgroup per row group leaves some CUs two row groups and others
                 // one (measured: 70B TP=4 at 1 token 51.4 -> 48 us; the 7B TP=2 shard, 352 KB per
                 // CU, is faster with one workgroup per row group).
                 if (4 * d.N * d.K >= (int64_t)device_cus() * (640 << 10))
-                    return run_bias<1, 2, 8, TP_SKINNY_U1, true, kActSwiglu>(d, stream);
+                    return run_bias<1, 2, 8, TP_SKINNY_U1, true, kActSwiglu>(d, c);
                 // Shorter streams: two 32-wide K steps per piece (measured: 7B TP=2 gate/up at 1
                 // token 25.2 -> 24.2 us; four steps stay best for the plain products).
-                return run_bias<1, 2, 8, 2, false, kActSwiglu>(d, stream);
+                return run_bias<1, 2, 8, 2, false, kActSwiglu>(d, c);
             case 2:  // the same choice for two token tiles (measured: 70B TP=4 at 32 tokens 68 -> 61 us)
                 if (ceil_div(d.N, 32) * 5 >= (int64_t)device_cus() * 4)
-                    return run_bias<2, 4, 8, 2, false, kActSwiglu>(d, stream, true);
-                return run_bias<2, 2, 4, 2, false, kActSwiglu>(d, stream);
+                    return run_bias<2, 4, 8, 2, false, kActSwiglu>(d, c, true);
+                return run_bias<2, 2, 4, 2, false, kActSwiglu>(d, c);
             case 3:  // three token tiles run as four: 1 + 1 tiles per wave reload tokens more than the
                      // padded rows cost (measured: 70B TP=4 at 48 tokens 79 -> 63 us, 7B TP=2 42 -> 35 us)
-                return run_bias<4, 4, 4, TP_SKINNY_U4, true, kActSwiglu>(d, stream);
-            case 4: return run_bias<4, 4, 4, TP_SKINNY_U4, true, kActSwiglu>(d, stream);
+                return run_bias<4, 4, 4, TP_SKINNY_U4, true, kActSwiglu>(d, c);
+            case 4: return run_bias<4, 4, 4, TP_SKINNY_U4, true, kActSwiglu>(d, c);
             default: return TP_ERR_SHAPE;
         }
     }
@@ -417,11 +422,11 @@ tp_status_t launch_skinny(const LinearDesc& d, hipStream_t stream) {
             case 1:
                 // From TP_SKINNY_M2 tokens on, two row tiles per token load halve the token
                 // reloads (measured: 70B TP=4 down at 16 tokens 34 -> 26 us).
-                if (d.M >= TP_SKINNY_M2) return run_bias<1, 2, 8, 2, false, A>(d, stream);
-                return run_bias<1, 1, 8, TP_SKINNY_U1, false, A>(d, stream);
-            case 2: return run_bias<2, 2, 4, 2, false, A>(d, stream);
-            case 3: return run_bias<3, 2, 4, 2, false, A>(d, stream);
-            case 4: return run_bias<4, 4, 4, TP_SKINNY_U4, true, A>(d, stream);
+                if (d.M >= TP_SKINNY_M2) return run_bias<1, 2, 8, 2, false, A>(d, c);
+                return run_bias<1, 1, 8, TP_SKINNY_U1, false, A>(d, c);
+            case 2: return run_bias<2, 2, 4, 2, false, A>(d, c);
+            case 3: return run_bias<3, 2, 4, 2, false, A>(d, c);
+            case 4: return run_bias<4, 4, 4, TP_SKINNY_U4, true, A>(d, c);
             default: return TP_ERR_SHAPE;
         }
     };

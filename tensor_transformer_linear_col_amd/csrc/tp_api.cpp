@@ -38,14 +38,22 @@ tp_status_t check_dims(int64_t M, std::initializer_list<int64_t> pos) {
         if (st_ != TP_OK) return st_;      \
     } while (0)
 
-tp_status_t launch_linear(const LinearDesc& d, hipStream_t s) {
+tp_status_t launch_linear(const LinearDesc& d, const Ctx& c) {
     if (d.M == 0) return TP_OK;
-    if (d.in_dtype == TP_DTYPE_F32) return launch_f32(d, s);
-    if (d.M <= 64) return launch_skinny(d, s);
-    return launch_gemm(d, s);
+    if (d.in_dtype == TP_DTYPE_F32) return launch_f32(d, c);
+    if (d.M <= 64) return launch_skinny(d, c);
+    return launch_gemm(d, c);
 }
 
-// ---- work space cache: one per (device, stream) --------------------------------------
+// KV heads a shard holds: G/p when p divides G; one (replicated on p/G consecutive
+// shards) when p is a multiple of G; 0 (invalid) otherwise.
+int64_t kv_heads_per_shard(int64_t n_kv_heads, int64_t p) {
+    if (n_kv_heads % p == 0) return n_kv_heads / p;
+    if (p % n_kv_heads == 0) return 1;
+    return 0;
+}
+
+// ---- work space: reserved by the caller, one per (device, stream) -------------------
 struct WsEntry {
     void* base = nullptr;
     size_t partial_floats = 0;
@@ -57,46 +65,52 @@ std::map<std::pair<int, hipStream_t>, WsEntry> g_ws;
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// KV heads a shard holds: G/p when p divides G; one (replicated on p/G consecutive
-// shards) when p is a multiple of G; 0 (invalid) otherwise.
-int64_t kv_heads_per_shard(int64_t n_kv_heads, int64_t p) {
-    if (n_kv_heads % p == 0) return n_kv_heads / p;
-    if (p % n_kv_heads == 0) return 1;
-    return 0;
+// Dry run (tp_plan_begin .. tp_plan_end) of this host thread: calls validate and
+// record the largest work space any of them needs, and enqueue nothing.
+thread_local bool t_planning = false;
+thread_local WsNeed t_plan;
+
+Workspace view_of(const WsEntry& e) {
+    Workspace w;
+    w.counters = static_cast<unsigned*>(e.base);
+    w.n_counters = e.counters;
+    w.partials = reinterpret_cast<float*>(static_cast<char*>(e.base) + round_up(e.counters * sizeof(unsigned), 256));
+    w.partial_floats = e.partial_floats;
+    return w;
 }
 
-}  // namespace
-
-namespace tp {
-
-tp_status_t get_workspace(hipStream_t stream, size_t partial_floats, size_t n_counters, Workspace* out) {
+// The reserved work space of the current device and `stream`, if it covers `need`.
+tp_status_t find_workspace(hipStream_t stream, const WsNeed& need, Workspace* out) {
+    *out = Workspace{};
+    if (need.empty()) return TP_OK;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return TP_ERR_HIP;
     std::lock_guard<std::mutex> lock(g_ws_mu);
-    WsEntry& e = g_ws[{dev, stream}];
-    if (e.base == nullptr || e.partial_floats < partial_floats || e.counters < n_counters) {
-        const size_t want_f = std::max(e.partial_floats, round_up(partial_floats, 1 << 16));
-        const size_t want_c = std::max(e.counters, round_up(n_counters, 1 << 12));
-        if (e.base) {
-            // Work still queued on this stream may use the old buffer.
-            if (hipStreamSynchronize(stream) != hipSuccess) return TP_ERR_HIP;
-            if (hipFree(e.base) != hipSuccess) return TP_ERR_HIP;
-            e.base = nullptr;
-        }
-        void* p = nullptr;
-        if (hipMalloc(&p, want_c * sizeof(unsigned) + want_f * sizeof(float)) != hipSuccess) return TP_ERR_HIP;
-        e.base = p;
-        e.partial_floats = want_f;
-        e.counters = want_c;
-        // Counters start at zero; every split-K tile resets its own counter when done.
-        TP_TRY(launch_fill_u32(static_cast<unsigned*>(p), want_c, 0u, stream));
-    }
-    out->counters = static_cast<unsigned*>(e.base);
-    out->partials = reinterpret_cast<float*>(static_cast<unsigned*>(e.base) + e.counters);
-    return TP_OK;
+    auto it = g_ws.find({dev, stream});
+    if (it == g_ws.end() || it->second.base == nullptr) return TP_ERR_WORKSPACE;
+    *out = view_of(it->second);
+    return out->covers(need) ? TP_OK : TP_ERR_WORKSPACE;
 }
 
-}  // namespace tp
+// Runs an entry point's launches: first all of them in plan mode (every check, the
+// work space they need; nothing enqueued), then, unless this thread is planning, all
+// of them for real. So a call that fails enqueues nothing.
+template <typename Body>
+tp_status_t planned(hipStream_t stream, Body&& body) {
+    WsNeed need;
+    const Ctx plan{stream, nullptr, &need};
+    TP_TRY(body(plan));
+    if (t_planning) {
+        t_plan.merge(need);
+        return TP_OK;
+    }
+    Workspace ws;
+    TP_TRY(find_workspace(stream, need, &ws));
+    const Ctx go{stream, &ws, nullptr};
+    return body(go);
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -109,6 +123,9 @@ const char* tp_status_string(tp_status_t s) {
         case TP_ERR_DTYPE: return "TP_ERR_DTYPE: unsupported dtype combination";
         case TP_ERR_ALIGN: return "TP_ERR_ALIGN: a bf16 operand or its row stride is not 16-byte aligned";
         case TP_ERR_HIP: return "TP_ERR_HIP: the HIP runtime reported an error";
+        case TP_ERR_WORKSPACE:
+            return "TP_ERR_WORKSPACE: the work space reserved for this device and stream is too small "
+                   "(size it with tp_plan_begin/tp_plan_end, reserve it with tp_workspace_reserve)";
     }
     return "unknown tp_status_t";
 }
@@ -124,8 +141,8 @@ tp_status_t tp_linear_col(const void* X, const void* W_r, const void* b_r, void*
     const int64_t n = out_features / tp_size;
     TP_TRY(check_vec_operand(X, in_features, dtype));
     TP_TRY(check_vec_operand(W_r, in_features, dtype));
-    LinearDesc d{X, in_features, W_r, nullptr, b_r, nullptr, Y_r, n, M, n, in_features, dtype, dtype, false};
-    return launch_linear(d, static_cast<hipStream_t>(stream));
+    const LinearDesc d{X, in_features, W_r, nullptr, b_r, nullptr, Y_r, n, M, n, in_features, dtype, dtype, false};
+    return planned(static_cast<hipStream_t>(stream), [&](const Ctx& c) { return launch_linear(d, c); });
 }
 
 tp_status_t tp_linear_row_partial(const void* X_r, int64_t ldx, const void* W_r, void* P_r, int64_t M,
@@ -141,9 +158,9 @@ tp_status_t tp_linear_row_partial(const void* X_r, int64_t ldx, const void* W_r,
     if (ldx < k) return TP_ERR_SHAPE;
     TP_TRY(check_vec_operand(X_r, ldx, dtype));
     TP_TRY(check_vec_operand(W_r, k, dtype));
-    LinearDesc d{X_r, ldx, W_r, nullptr, nullptr, nullptr, P_r, out_features, M, out_features, k, dtype,
-                 partial_dtype, false};
-    return launch_linear(d, static_cast<hipStream_t>(stream));
+    const LinearDesc d{X_r, ldx, W_r, nullptr, nullptr, nullptr, P_r, out_features, M, out_features, k, dtype,
+                       partial_dtype, false};
+    return planned(static_cast<hipStream_t>(stream), [&](const Ctx& c) { return launch_linear(d, c); });
 }
 
 tp_status_t tp_mlp_shard(const void* X, const void* Wg_r, const void* Wu_r, const void* bg_r, const void* bu_r,
@@ -165,12 +182,12 @@ tp_status_t tp_mlp_shard(const void* X, const void* Wg_r, const void* Wu_r, cons
         TP_TRY(check_vec_operand(H_r, i, dtype));
         TP_TRY(check_vec_operand(Wd_r, i, dtype));
     }
-    const hipStream_t s = static_cast<hipStream_t>(stream);
-    LinearDesc up{X, hidden, Wg_r, Wu_r, bg_r, bu_r, H_r, i, M, i, hidden, dtype, dtype, true};
-    TP_TRY(launch_linear(up, s));
-    if (!P_r) return TP_OK;
-    LinearDesc down{H_r, i, Wd_r, nullptr, nullptr, nullptr, P_r, hidden, M, hidden, i, dtype, partial_dtype, false};
-    return launch_linear(down, s);
+    const LinearDesc up{X, hidden, Wg_r, Wu_r, bg_r, bu_r, H_r, i, M, i, hidden, dtype, dtype, true};
+    const LinearDesc down{H_r, i, Wd_r, nullptr, nullptr, nullptr, P_r, hidden, M, hidden, i, dtype, partial_dtype, false};
+    return planned(static_cast<hipStream_t>(stream), [&](const Ctx& c) {
+        TP_TRY(launch_linear(up, c));
+        return P_r ? launch_linear(down, c) : TP_OK;
+    });
 }
 
 tp_status_t tp_ffn_gelu_shard(const void* X, const void* W1_r, const void* b1_r, const void* W2_r, void* H_r,
@@ -190,12 +207,12 @@ tp_status_t tp_ffn_gelu_shard(const void* X, const void* W1_r, const void* b1_r,
         TP_TRY(check_vec_operand(H_r, i, dtype));
         TP_TRY(check_vec_operand(W2_r, i, dtype));
     }
-    const hipStream_t s = static_cast<hipStream_t>(stream);
-    LinearDesc up{X, hidden, W1_r, nullptr, b1_r, nullptr, H_r, i, M, i, hidden, dtype, dtype, false, true};
-    TP_TRY(launch_linear(up, s));
-    if (!P_r) return TP_OK;
-    LinearDesc down{H_r, i, W2_r, nullptr, nullptr, nullptr, P_r, hidden, M, hidden, i, dtype, partial_dtype, false};
-    return launch_linear(down, s);
+    const LinearDesc up{X, hidden, W1_r, nullptr, b1_r, nullptr, H_r, i, M, i, hidden, dtype, dtype, false, true};
+    const LinearDesc down{H_r, i, W2_r, nullptr, nullptr, nullptr, P_r, hidden, M, hidden, i, dtype, partial_dtype, false};
+    return planned(static_cast<hipStream_t>(stream), [&](const Ctx& c) {
+        TP_TRY(launch_linear(up, c));
+        return P_r ? launch_linear(down, c) : TP_OK;
+    });
 }
 
 tp_status_t tp_attn_proj_shard(const void* X, const void* Wqkv_r, const void* bqkv_r, void* QKV_r, const void* A_r,
@@ -222,15 +239,12 @@ tp_status_t tp_attn_proj_shard(const void* X, const void* Wqkv_r, const void* bq
         TP_TRY(check_vec_operand(A_r, ka, dtype));
         TP_TRY(check_vec_operand(Wo_r, ka, dtype));
     }
-    if (QKV_r) {
-        LinearDesc q{X, hidden, Wqkv_r, nullptr, bqkv_r, nullptr, QKV_r, nqkv, M, nqkv, hidden, dtype, dtype, false};
-        TP_TRY(launch_linear(q, s));
-    }
-    if (P_r) {
-        LinearDesc o{A_r, ka, Wo_r, nullptr, nullptr, nullptr, P_r, hidden, M, hidden, ka, dtype, partial_dtype, false};
-        TP_TRY(launch_linear(o, s));
-    }
-    return TP_OK;
+    const LinearDesc q{X, hidden, Wqkv_r, nullptr, bqkv_r, nullptr, QKV_r, nqkv, M, nqkv, hidden, dtype, dtype, false};
+    const LinearDesc o{A_r, ka, Wo_r, nullptr, nullptr, nullptr, P_r, hidden, M, hidden, ka, dtype, partial_dtype, false};
+    return planned(s, [&](const Ctx& c) {
+        if (QKV_r) TP_TRY(launch_linear(q, c));
+        return P_r ? launch_linear(o, c) : TP_OK;
+    });
 }
 
 tp_status_t tp_attn_core_shard(const void* QKV_r, void* A_r, int64_t M, int32_t n_heads, int32_t n_kv_heads,
@@ -247,8 +261,9 @@ tp_status_t tp_attn_core_shard(const void* QKV_r, void* A_r, int64_t M, int32_t 
     TP_TRY(check_vec_operand(QKV_r, ldq, dtype));
     TP_TRY(check_vec_operand(A_r, lda, dtype));
     if (M == 0) return TP_OK;
-    return launch_attn_core(QKV_r, ldq, A_r, lda, M, (int)hq, (int)hk, head_dim, causal != 0,
-                            static_cast<hipStream_t>(stream));
+    return planned(static_cast<hipStream_t>(stream), [&](const Ctx& c) {
+        return launch_attn_core(QKV_r, ldq, A_r, lda, M, (int)hq, (int)hk, head_dim, causal != 0, c);
+    });
 }
 
 tp_status_t tp_attn_decode_shard(const void* QKV_r, void* K_cache_r, void* V_cache_r, int64_t cache_len,
@@ -271,8 +286,10 @@ tp_status_t tp_attn_decode_shard(const void* QKV_r, void* K_cache_r, void* V_cac
     // The kernel addresses the used part of a cache with 32-bit byte offsets.
     if ((cache_len + M) * ldkv * 2 >= (int64_t(1) << 31)) return TP_ERR_SHAPE;
     if (M == 0) return TP_OK;
-    return launch_attn_decode(QKV_r, ldq, K_cache_r, V_cache_r, ldkv, cache_len, A_r, lda, M, (int)hq, (int)hk,
-                              head_dim, static_cast<hipStream_t>(stream));
+    return planned(static_cast<hipStream_t>(stream), [&](const Ctx& c) {
+        return launch_attn_decode(QKV_r, ldq, K_cache_r, V_cache_r, ldkv, cache_len, A_r, lda, M, (int)hq, (int)hk,
+                                  head_dim, c);
+    });
 }
 
 tp_status_t tp_combine_concat(const void* const* shards, int32_t tp_size, const int64_t* seg_widths, int32_t nseg,
@@ -284,6 +301,7 @@ tp_status_t tp_combine_concat(const void* const* shards, int32_t tp_size, const 
         if (!shards[r]) return TP_ERR_NULL;
     for (int32_t j = 0; j < nseg; ++j)
         if (seg_widths[j] <= 0 || seg_widths[j] > kMaxDim) return TP_ERR_SHAPE;
+    if (t_planning) return TP_OK;
     return launch_concat(shards, tp_size, seg_widths, nseg, Y, M, elem_size(dtype), static_cast<hipStream_t>(stream));
 }
 
@@ -295,6 +313,7 @@ tp_status_t tp_combine_sum(const void* const* partials, int32_t tp_size, tp_dtyp
     if (tp_size < 1 || tp_size > kMaxTP) return TP_ERR_SHAPE;
     for (int32_t r = 0; r < tp_size; ++r)
         if (!partials[r]) return TP_ERR_NULL;
+    if (t_planning) return TP_OK;
     return launch_combine_sum(partials, tp_size, partial_dtype, b, Y, M, N, out_dtype,
                               static_cast<hipStream_t>(stream));
 }
@@ -306,15 +325,15 @@ tp_status_t tp_shard_weight(const void* W, int64_t out_features, int64_t in_feat
     TP_TRY(check_dims(0, {out_features, in_features}));
     if (tp_size < 1 || tp_size > kMaxTP || rank < 0 || rank >= tp_size || (axis != 0 && axis != 1))
         return TP_ERR_SHAPE;
+    if ((axis == 0 ? out_features : in_features) % tp_size != 0) return TP_ERR_INDIVISIBLE;
+    if (t_planning) return TP_OK;
     const size_t es = elem_size(dtype);
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (axis == 0) {
-        if (out_features % tp_size != 0) return TP_ERR_INDIVISIBLE;
         const int64_t rows = out_features / tp_size;
         const char* src = static_cast<const char*>(W) + (size_t)(rank * rows) * in_features * es;
         return launch_copy2d(src, in_features, W_r, in_features, rows, in_features, es, s);
     }
-    if (in_features % tp_size != 0) return TP_ERR_INDIVISIBLE;
     const int64_t cols = in_features / tp_size;
     const char* src = static_cast<const char*>(W) + (size_t)(rank * cols) * es;
     return launch_copy2d(src, in_features, W_r, cols, out_features, cols, es, s);
@@ -328,6 +347,7 @@ tp_status_t tp_shard_weight_block(const void* W, int64_t out_features, int64_t i
     if ((axis != 0 && axis != 1) || start < 0 || width <= 0) return TP_ERR_SHAPE;
     const int64_t n = axis == 0 ? out_features : in_features;
     if (start + width > n) return TP_ERR_SHAPE;
+    if (t_planning) return TP_OK;
     const size_t es = elem_size(dtype);
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (axis == 0) {
@@ -350,7 +370,7 @@ tp_status_t tp_combine_concat_v(const void* const* shards, int32_t n_shards, con
         total += widths[r];
     }
     if (total > kMaxDim) return TP_ERR_SHAPE;
-    if (M == 0) return TP_OK;
+    if (M == 0 || t_planning) return TP_OK;
     const size_t es = elem_size(dtype);
     const hipStream_t s = static_cast<hipStream_t>(stream);
     int64_t col = 0;
@@ -368,6 +388,7 @@ tp_status_t tp_shard_qkv(const void* Wqkv, int64_t in_features, int32_t n_heads,
     TP_TRY(check_dims(0, {in_features, n_heads, n_kv_heads, head_dim}));
     if (tp_size < 1 || tp_size > kMaxTP || rank < 0 || rank >= tp_size) return TP_ERR_SHAPE;
     if (n_heads % tp_size != 0 || kv_heads_per_shard(n_kv_heads, tp_size) == 0) return TP_ERR_INDIVISIBLE;
+    if (t_planning) return TP_OK;
     const size_t es = elem_size(dtype);
     const int64_t d = head_dim, hq = n_heads / tp_size, hk = kv_heads_per_shard(n_kv_heads, tp_size);
     // First KV head of the shard: rank*hk when p divides G, else rank*G/p (replicated).
@@ -382,6 +403,62 @@ tp_status_t tp_shard_qkv(const void* Wqkv, int64_t in_features, int32_t n_heads,
         TP_TRY(launch_copy2d(src, in_features, dst, in_features, nrows[j], in_features, es, s));
         dst_row += nrows[j];
     }
+    return TP_OK;
+}
+
+tp_status_t tp_workspace_reserve(void* stream, size_t partial_bytes, size_t n_counters) {
+    if (t_planning) return TP_OK;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return TP_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    WsEntry& e = g_ws[{dev, s}];
+    const size_t want_f = std::max(e.partial_floats, round_up(partial_bytes, 256) / sizeof(float));
+    const size_t want_c = std::max(e.counters, round_up(std::max<size_t>(n_counters, 1), 64));
+    if (e.base && e.partial_floats >= want_f && e.counters >= want_c) return TP_OK;
+    if (e.base) {
+        // Work still queued on this stream may use the old space.
+        if (hipStreamSynchronize(s) != hipSuccess) return TP_ERR_HIP;
+        if (hipFree(e.base) != hipSuccess) return TP_ERR_HIP;
+        e = WsEntry{};
+    }
+    void* p = nullptr;
+    if (hipMalloc(&p, round_up(want_c * sizeof(unsigned), 256) + want_f * sizeof(float)) != hipSuccess)
+        return TP_ERR_HIP;
+    e.base = p;
+    e.partial_floats = want_f;
+    e.counters = want_c;
+    // Counters start at zero; every launch that uses one leaves it at zero.
+    return launch_fill_u32(static_cast<unsigned*>(p), want_c, 0u, s);
+}
+
+tp_status_t tp_workspace_reserved(void* stream, size_t* partial_bytes, size_t* n_counters) {
+    if (!partial_bytes || !n_counters) return TP_ERR_NULL;
+    *partial_bytes = 0;
+    *n_counters = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return TP_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    auto it = g_ws.find({dev, static_cast<hipStream_t>(stream)});
+    if (it != g_ws.end() && it->second.base) {
+        *partial_bytes = it->second.partial_floats * sizeof(float);
+        *n_counters = it->second.counters;
+    }
+    return TP_OK;
+}
+
+tp_status_t tp_plan_begin(void) {
+    t_planning = true;
+    t_plan = WsNeed{};
+    return TP_OK;
+}
+
+tp_status_t tp_plan_end(size_t* partial_bytes, size_t* n_counters) {
+    const WsNeed n = t_plan;
+    t_planning = false;
+    t_plan = WsNeed{};
+    if (partial_bytes) *partial_bytes = n.partial_floats * sizeof(float);
+    if (n_counters) *n_counters = n.counters;
     return TP_OK;
 }
 

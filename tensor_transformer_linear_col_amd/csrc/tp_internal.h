@@ -32,28 +32,50 @@ struct LinearDesc {
     bool gelu = false;  // plain products only: y = gelu(XW^T + b), erf form
 };
 
-// Split-K work space: fp32 partial tiles and per-tile arrival counters.
-struct Workspace {
-    float* partials;
-    unsigned* counters;
+// Work space of the kernels that split a reduction across workgroups: fp32 partial
+// sums and arrival counters (every counter is zero between launches: the last
+// workgroup to arrive resets its own).
+struct WsNeed {
+    size_t partial_floats = 0;
+    size_t counters = 0;
+    void merge(const WsNeed& o) {
+        if (o.partial_floats > partial_floats) partial_floats = o.partial_floats;
+        if (o.counters > counters) counters = o.counters;
+    }
+    bool empty() const { return partial_floats == 0 && counters == 0; }
 };
 
-// Returns the work space for the current device and `stream`, at least the given sizes.
-tp_status_t get_workspace(hipStream_t stream, size_t partial_floats, size_t n_counters,
-                          Workspace* out);
+struct Workspace {
+    float* partials = nullptr;
+    size_t partial_floats = 0;
+    unsigned* counters = nullptr;
+    size_t n_counters = 0;
+    bool covers(const WsNeed& n) const { return partial_floats >= n.partial_floats && n_counters >= n.counters; }
+};
 
-// Kernel launchers (each validates nothing: the C ABI layer has done it).
-tp_status_t launch_skinny(const LinearDesc& d, hipStream_t stream);
-tp_status_t launch_gemm(const LinearDesc& d, hipStream_t stream);
-tp_status_t launch_f32(const LinearDesc& d, hipStream_t stream);
+// How a launcher is called. Plan mode (need != nullptr): check everything that could
+// make the launch fail and record the work space it needs, enqueue nothing. Launch
+// mode (need == nullptr): enqueue on `stream`, taking scratch memory from *ws, which the
+// caller has sized from the plan.
+struct Ctx {
+    hipStream_t stream;
+    const Workspace* ws;
+    WsNeed* need;
+    bool planning() const { return need != nullptr; }
+};
+
+// Kernel launchers (the C ABI layer has validated the arguments).
+tp_status_t launch_skinny(const LinearDesc& d, const Ctx& c);
+tp_status_t launch_gemm(const LinearDesc& d, const Ctx& c);
+tp_status_t launch_f32(const LinearDesc& d, const Ctx& c);
 // Head-local attention core: out[M, hq*d] (row stride lda) from qkv[M, (hq+2hk)*d] (row stride ldq).
 tp_status_t launch_attn_core(const void* qkv, int64_t ldq, void* out, int64_t lda, int64_t M, int hq, int hk, int d,
-                             bool causal, hipStream_t stream);
+                             bool causal, const Ctx& c);
 // One decode step: appends the M new tokens' K and V rows of qkv[M, ldq] (Q segment first) to
 // the caches kc/vc[.., ldkv] at row cache_len, then attention of the new tokens (positions
 // cache_len ..) over cache_len + M keys, causal; out[M, hq*d] (row stride lda).
 tp_status_t launch_attn_decode(const void* qkv, int64_t ldq, void* kc, void* vc, int64_t ldkv, int64_t cache_len,
-                               void* out, int64_t lda, int64_t M, int hq, int hk, int d, hipStream_t stream);
+                               void* out, int64_t lda, int64_t M, int hq, int hk, int d, const Ctx& c);
 
 tp_status_t launch_combine_sum(const void* const* partials, int p, tp_dtype_t pdt, const void* b,
                                void* Y, int64_t M, int64_t N, tp_dtype_t odt, hipStream_t stream);

@@ -27,6 +27,27 @@ def pytest_collection_modifyitems(config, items):
             item.add_marker(skip)
 
 
+# Work space reserved once for the null stream, which every GPU test uses unless it says
+# otherwise: enough for every split reduction the tests run (the largest, a split-K of up
+# to 255 partial tiles of 256 x 256 fp32, is 255 MiB).
+TEST_WORKSPACE_BYTES = 256 << 20
+TEST_WORKSPACE_COUNTERS = 1 << 20
+
+
+@pytest.fixture(autouse=True, scope="session")
+def _reserve_workspace():
+    try:
+        import torch
+        has_gpu = torch.cuda.is_available()
+    except Exception:  # pragma: no cover
+        has_gpu = False
+    if has_gpu:
+        import tensor_transformer_linear_col_amd as tp
+        tp.tp_workspace_reserve(TEST_WORKSPACE_BYTES, TEST_WORKSPACE_COUNTERS)
+        torch.cuda.synchronize()
+    yield
+
+
 def golden_path(name: str) -> str:
     return os.path.join(ROOT, "tests", "golden", name)
 

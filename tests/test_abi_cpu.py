@@ -12,7 +12,7 @@ import tensor_transformer_linear_col_amd as tp
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "tp_linear.h")
 
-OK, NULL, SHAPE, INDIV, DTYPE, ALIGN, HIP = range(7)
+OK, NULL, SHAPE, INDIV, DTYPE, ALIGN, HIP, WORKSPACE = range(8)
 F32, BF16 = 0, 1
 P = 0x100000  # a 16-byte aligned fake device address, never dereferenced
 
@@ -31,17 +31,17 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 19, names
     for name in names:
         assert hasattr(L, name), name
     assert set(names) == set(tp.EXPORTS)
 
 
 def test_status_strings(L):
-    for code in range(7):
+    for code in range(8):
         assert tp.tp_status_string(code).startswith(
             ["TP_OK", "TP_ERR_NULL", "TP_ERR_SHAPE", "TP_ERR_INDIVISIBLE", "TP_ERR_DTYPE",
-             "TP_ERR_ALIGN", "TP_ERR_HIP"][code])
+             "TP_ERR_ALIGN", "TP_ERR_HIP", "TP_ERR_WORKSPACE"][code])
     assert "unknown" in tp.tp_status_string(99)
 
 
@@ -217,3 +217,103 @@ def test_binding_rejects_host_tensors():
     x = torch.zeros(1, 8)
     with pytest.raises(ValueError):
         tp.tp_linear_col(x, x, None, x, 1, 8, 6, 2)
+
+
+# ---- work space: sized by a dry run, reserved by the caller, never allocated by a call ----
+
+def _plan(L, fn):
+    """Dry run of fn(): its status and the work space (partial bytes, counters) it plans."""
+    a, b = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert L.tp_plan_begin() == OK
+    try:
+        st = fn()
+    finally:
+        assert L.tp_plan_end(ctypes.byref(a), ctypes.byref(b)) == OK
+    return st, a.value, b.value
+
+
+def test_dry_run_sizes_the_split_reductions(L):
+    """A dry run validates, enqueues nothing (no GPU here, so any launch would fail with
+    TP_ERR_HIP) and reports the largest work space of the calls inside it. Without a device
+    the library plans for 256 compute units, as on MI355X."""
+    # 70B QKV shard at TP = 8 and 4096 tokens: 5 x 16 = 80 tiles of 256 x 256 on 256 CUs, each
+    # cut into 3 K ranges -> 240 fp32 partial tiles of 256 KB.
+    qkv = lambda: L.tp_attn_proj_shard(P, P, 0, P, 0, 0, 0, 4096, 8192, 64, 8, 128, 8, BF16, BF16, None)
+    assert _plan(L, qkv) == (OK, 240 * 256 * 256 * 4, 0)
+    # The same QKV shard at one token: 80 row groups of 16 outputs, K cut in 4 -> 320
+    # workgroups with two 1 KB partial tiles each, and one arrival counter per row group.
+    qkv1 = lambda: L.tp_attn_proj_shard(P, P, 0, P, 0, 0, 0, 1, 8192, 64, 8, 128, 8, BF16, BF16, None)
+    assert _plan(L, qkv1) == (OK, 320 * 2 * 256 * 4, 80)
+    # Products that split nothing need no work space; M = 0 does nothing at all.
+    gateup = lambda: L.tp_mlp_shard(P, P, P, 0, 0, P, P, P, 4096, 8192, 28672, 8, BF16, BF16, None)
+    assert _plan(L, gateup) == (OK, 0, 0)
+    assert _plan(L, lambda: col(L, M=0)) == (OK, 0, 0)
+    # Several calls: the largest need of any of them.
+    both = lambda: (qkv1(), qkv(), gateup())[-1]
+    assert _plan(L, both) == (OK, 240 * 256 * 256 * 4, 80)
+    # Validation still applies inside a dry run.
+    assert _plan(L, lambda: col(L, X=0))[0] == NULL
+
+
+def test_multi_launch_call_rejects_before_its_first_launch(L):
+    """tp_mlp_shard whose gate/up product is fine but whose down product would need 32-bit
+    offsets past 4 GiB (M x I/p x 2 bytes) is rejected as a whole before anything is
+    enqueued: it returns TP_ERR_SHAPE, not the TP_ERR_HIP a launch attempt gives here."""
+    M, hidden, inter = 1 << 20, 1024, 2048
+    st = L.tp_mlp_shard(P, P, P, 0, 0, P, P, P, M, hidden, inter, 1, BF16, BF16, None)
+    assert st == SHAPE
+    # Without the down product the same call plans fine (and then needs the GPU).
+    assert _plan(L, lambda: L.tp_mlp_shard(P, P, P, 0, 0, 0, P, 0, M, hidden, inter, 1, BF16, BF16, None)) == (OK, 0, 0)
+
+
+def test_workspace_calls_without_a_device(L):
+    a, b = ctypes.c_size_t(7), ctypes.c_size_t(7)
+    assert L.tp_workspace_reserved(None, ctypes.byref(a), ctypes.byref(b)) in (OK, HIP)
+    assert L.tp_workspace_reserved(None, None, ctypes.byref(b)) == NULL
+    # Inside a dry run a reservation does nothing (and needs no device).
+    assert _plan(L, lambda: L.tp_workspace_reserve(None, 1 << 20, 64)) == (OK, 0, 0)
+
+
+def test_binding_rejects_mismatched_dtypes_before_any_device_access():
+    """Each wrapper passes one dtype per role to the library; a tensor of another width
+    would be read or written out of bounds, so it raises TypeError first (CPU tensors
+    suffice: the dtype check precedes the device checks)."""
+    import torch
+    f, b = torch.float32, torch.bfloat16
+    t = lambda *shape, dt=b: torch.zeros(*shape, dtype=dt)
+    with pytest.raises(TypeError, match="W_r"):
+        tp.tp_linear_col(t(2, 8, dt=f), t(3, 8), None, t(2, 3, dt=f), 2, 8, 6, 2)
+    with pytest.raises(TypeError, match="Y_r"):
+        tp.tp_linear_col(t(2, 8), t(3, 8), None, t(2, 3, dt=f), 2, 8, 6, 2)
+    with pytest.raises(TypeError, match="b_r"):
+        tp.tp_linear_col(t(2, 8), t(3, 8), t(3, dt=f), t(2, 3), 2, 8, 6, 2)
+    with pytest.raises(TypeError, match="X_r"):
+        tp.tp_linear_row_partial(t(2, 4, dt=f), 4, t(6, 4), t(2, 6), 2, 8, 6, 2)
+    with pytest.raises(TypeError, match="P_r"):
+        tp.tp_linear_row_partial(t(2, 4), 4, t(6, 4), t(2, 6, dt=f), 2, 8, 6, 2, partial_dtype=tp.TP_DTYPE_BF16)
+    with pytest.raises(TypeError, match="H_r"):
+        tp.tp_mlp_shard(t(2, 8), t(4, 8), t(4, 8), None, None, None, t(2, 4, dt=f), None, 2, 8, 8, 2)
+    with pytest.raises(TypeError, match="Wu_r"):
+        tp.tp_mlp_shard(t(2, 8), t(4, 8), t(4, 8, dt=f), None, None, None, t(2, 4), None, 2, 8, 8, 2)
+    with pytest.raises(TypeError, match="W2_r"):
+        tp.tp_ffn_gelu_shard(t(2, 8), t(4, 8), None, t(8, 4, dt=f), t(2, 4), t(2, 8), 2, 8, 8, 2)
+    with pytest.raises(TypeError, match="Wo_r"):
+        tp.tp_attn_proj_shard(None, None, None, None, t(2, 16), t(8, 16, dt=f), t(2, 8), 2, 8, 2, 2, 8, 1)
+    with pytest.raises(TypeError, match="partials"):
+        tp.tp_combine_sum([t(2, 8), t(2, 8, dt=f)], None, t(2, 8), 2, 8)
+    with pytest.raises(TypeError, match="b"):
+        tp.tp_combine_sum([t(2, 8), t(2, 8)], t(8, dt=f), t(2, 8), 2, 8)
+    with pytest.raises(TypeError, match="shards"):
+        tp.tp_combine_concat([t(2, 8), t(2, 8, dt=f)], [8], t(2, 16), 2)
+    with pytest.raises(TypeError, match="shards"):
+        tp.tp_combine_concat_v([t(2, 8, dt=f), t(2, 8)], [8, 8], t(2, 16), 2)
+    with pytest.raises(TypeError, match="W_r"):
+        tp.tp_shard_weight(t(8, 8), 8, 8, 2, 0, 0, t(4, 8, dt=f))
+    with pytest.raises(TypeError, match="Wqkv_r"):
+        tp.tp_shard_qkv(t(48, 8), 8, 4, 2, 8, 2, 0, t(32, 8, dt=f))
+    with pytest.raises(TypeError, match="W_r"):
+        tp.tp_shard_weight_block(t(8, 8), 8, 8, 0, 0, 4, t(4, 8, dt=f))
+    with pytest.raises(TypeError, match="A_r"):
+        tp.tp_attn_core_shard(t(4, 256), t(4, 128, dt=f), 4, 2, 1, 64, 1)
+    with pytest.raises(TypeError, match="V_cache_r"):
+        tp.tp_attn_decode_shard(t(1, 256), t(8, 64), t(8, 64, dt=f), 0, t(1, 128), 1, 2, 1, 64, 1)

@@ -376,7 +376,7 @@ def test_errors_raise_before_launch():
 
 # ---- the large-tile LDS-DMA kernel: ragged token and feature tails ------------------------
 # It runs when 256 x 256 tiles (128 x 256 for SwiGLU) alone fill the chip and K is a
-# multiple of 64, so these shapes are large; the oracle checks sampled token rows.
+# multiple of 64, so these shapes are large; the oracle checks every token row.
 
 DMA_SHAPES = [  # (M, K, N): tails in M and N, K a multiple of 64
     (2100, 1024, 8168), (4096 + 33, 576, 8192 - 40), (8192, 128, 8192 + 8),
@@ -386,8 +386,8 @@ DMA_SHAPES = [  # (M, K, N): tails in M and N, K a multiple of 64
 
 
 def _sample_rows(M):
-    rng = np.random.default_rng(M)
-    return np.unique(np.concatenate([[0, M - 1], rng.choice(M, 6, replace=False)]))
+    """Every token row (the name is kept for the tests below)."""
+    return np.arange(M)
 
 
 @pytest.mark.parametrize("M,K,N", DMA_SHAPES)
