@@ -120,6 +120,25 @@ tp_status_t tp_mlp_shard(const void* X, const void* Wg_r, const void* Wu_r,
                          int32_t tp_size, tp_dtype_t dtype, tp_dtype_t partial_dtype,
                          void* stream);
 
+/* tp_mlp_shard for callers that cannot allocate device memory or reserve a work space
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, validation and results (bitwise) as tp_mlp_shard. Its split reductions
+ * take their partial sums and arrival counters from a fixed scratch array inside the
+ * library instead of the reserved work space: 16 MiB of partials and 65536 counters, one
+ * copy per GPU, held until the process ends (its address is looked up on the first call on
+ * each device). It calls no hipMalloc, hipFree or other allocating routine and needs no
+ * tp_workspace_reserve. It clears the counters it uses with a small kernel on `stream`
+ * before its launches. A call whose launches need more scratch than that (large prefill
+ * products split across workgroups) returns TP_ERR_WORKSPACE with nothing enqueued; on a
+ * 256-CU MI355X every decode size (M <= 64, up to 2^20 intermediate features per shard)
+ * fits. All calls on one GPU share the array: calls that overlap on
+ * one GPU (different streams, or several host threads) race and give wrong results. */
+tp_status_t tp_mlp_shard_noalloc(const void* X, const void* Wg_r, const void* Wu_r,
+                                 const void* bg_r, const void* bu_r, const void* Wd_r,
+                                 void* H_r, void* P_r, int64_t M, int64_t hidden, int64_t intermediate,
+                                 int32_t tp_size, tp_dtype_t dtype, tp_dtype_t partial_dtype,
+                                 void* stream);
+
 /* The pages' own FFN, shard r ([P3] "Implementing Tensor Parallelism with Hugging Face
  * Accelerate": a ColumnParallelLinear hidden -> intermediate, GELU, a RowParallelLinear
  * intermediate -> hidden; its example is 4096 -> 11008 -> 4096 at batch 4):

@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "TP_DTYPE_F32", "TP_DTYPE_BF16", "TPError", "lib", "lib_path", "tp_linear_col",
-    "tp_linear_row_partial", "tp_mlp_shard", "tp_ffn_gelu_shard", "tp_attn_proj_shard", "tp_combine_concat",
+    "tp_linear_row_partial", "tp_mlp_shard", "tp_mlp_shard_noalloc", "tp_ffn_gelu_shard", "tp_attn_proj_shard", "tp_combine_concat",
     "tp_combine_sum", "tp_shard_weight", "tp_shard_qkv", "tp_shard_weight_block", "tp_combine_concat_v",
     "kv_heads_per_shard", "tp_attn_core_shard", "tp_attn_decode_shard", "tp_release_workspaces",
     "tp_workspace_reserve", "tp_workspace_reserved", "tp_plan", "tp_status_string", "TP_ERR_WORKSPACE",
@@ -36,6 +36,7 @@ _SIGS = {
     "tp_linear_col": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp],
     "tp_linear_row_partial": [_vp, _i64, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp],
     "tp_mlp_shard": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp],
+    "tp_mlp_shard_noalloc": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp],
     "tp_ffn_gelu_shard": [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp],
     "tp_attn_proj_shard": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _i32, _i32, _i32,
                            _i32, _vp],
@@ -187,13 +188,13 @@ def tp_linear_row_partial(X_r, ldx: int, W_r, P_r, M: int, in_features: int, out
 
 
 def tp_mlp_shard(X, Wg_r, Wu_r, bg_r, bu_r, Wd_r, H_r, P_r, M: int, hidden: int, intermediate: int,
-                 tp_size: int, partial_dtype=None) -> None:
+                 tp_size: int, partial_dtype=None, _name: str = "tp_mlp_shard") -> None:
     """H_r = silu(X Wg_r^T + bg_r) * (X Wu_r^T + bu_r); P_r = H_r Wd_r^T (partial)."""
     i = _div(intermediate, tp_size)
     need = i is not None and M > 0
     dt = _same(_dt(X), Wg_r=Wg_r, Wu_r=Wu_r, bg_r=bg_r, bu_r=bu_r, Wd_r=Wd_r, H_r=H_r)
     pdt = _pdt(P_r, partial_dtype, dt)
-    _call("tp_mlp_shard",
+    _call(_name,
           _dev(X, "X", M * hidden if need else None),
           _dev(Wg_r, "Wg_r", i * hidden if need else None),
           _dev(Wu_r, "Wu_r", i * hidden if need else None),
@@ -203,6 +204,14 @@ def tp_mlp_shard(X, Wg_r, Wu_r, bg_r, bu_r, Wd_r, H_r, P_r, M: int, hidden: int,
           _dev(H_r, "H_r", M * i if need else None),
           _dev(P_r, "P_r", M * hidden if need else None),
           M, hidden, intermediate, tp_size, dt, pdt, _stream())
+
+
+def tp_mlp_shard_noalloc(X, Wg_r, Wu_r, bg_r, bu_r, Wd_r, H_r, P_r, M: int, hidden: int, intermediate: int,
+                         tp_size: int, partial_dtype=None) -> None:
+    """tp_mlp_shard without a reserved work space: its split reductions use the library's fixed
+    per-GPU scratch array (calls that overlap on one GPU race)."""
+    tp_mlp_shard(X, Wg_r, Wu_r, bg_r, bu_r, Wd_r, H_r, P_r, M, hidden, intermediate, tp_size, partial_dtype,
+                 _name="tp_mlp_shard_noalloc")
 
 
 def tp_ffn_gelu_shard(X, W1_r, b1_r, W2_r, H_r, P_r, M: int, hidden: int, intermediate: int,

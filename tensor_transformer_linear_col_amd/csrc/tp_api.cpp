@@ -110,6 +110,61 @@ tp_status_t planned(hipStream_t stream, Body&& body) {
     return body(go);
 }
 
+// Validation shared by tp_mlp_shard and its allocation-free variant.
+tp_status_t mlp_descs(const void* X, const void* Wg_r, const void* Wu_r, const void* bg_r, const void* bu_r,
+                      const void* Wd_r, void* H_r, void* P_r, int64_t M, int64_t hidden, int64_t intermediate,
+                      int32_t tp_size, tp_dtype_t dtype, tp_dtype_t partial_dtype, LinearDesc* up, LinearDesc* down) {
+    if (!X || !Wg_r || !Wu_r || !H_r) return TP_ERR_NULL;
+    if (P_r && !Wd_r) return TP_ERR_NULL;
+    if ((bg_r == nullptr) != (bu_r == nullptr)) return TP_ERR_NULL;
+    if (!dtype_ok(dtype) || !dtype_ok(partial_dtype)) return TP_ERR_DTYPE;
+    if (dtype == TP_DTYPE_F32 && partial_dtype != TP_DTYPE_F32) return TP_ERR_DTYPE;
+    TP_TRY(check_dims(M, {hidden, intermediate}));
+    if (tp_size < 1 || tp_size > kMaxTP) return TP_ERR_SHAPE;
+    if (intermediate % tp_size != 0) return TP_ERR_INDIVISIBLE;
+    const int64_t i = intermediate / tp_size;
+    TP_TRY(check_vec_operand(X, hidden, dtype));
+    TP_TRY(check_vec_operand(Wg_r, hidden, dtype));
+    TP_TRY(check_vec_operand(Wu_r, hidden, dtype));
+    if (P_r) {
+        TP_TRY(check_vec_operand(H_r, i, dtype));
+        TP_TRY(check_vec_operand(Wd_r, i, dtype));
+    }
+    *up = LinearDesc{X, hidden, Wg_r, Wu_r, bg_r, bu_r, H_r, i, M, i, hidden, dtype, dtype, true};
+    *down = LinearDesc{H_r, i, Wd_r, nullptr, nullptr, nullptr, P_r, hidden, M, hidden, i, dtype, partial_dtype, false};
+    return TP_OK;
+}
+
+// ---- scratch of the allocation-free entry point --------------------------------------
+// A fixed device array, one copy per GPU the library runs on, held until the process ends:
+// the arrival counters first, then the fp32 partial sums. In host code the array's name is
+// only a stand-in; its device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchCounters = size_t(1) << 16;
+constexpr size_t kScratchPartialBytes = size_t(16) << 20;
+constexpr size_t kScratchCounterBytes = kScratchCounters * sizeof(unsigned);
+static __device__ __align__(256) unsigned char scratch[kScratchCounterBytes + kScratchPartialBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+tp_status_t scratch_of_current_device(Workspace* out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TP_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return TP_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    char* base = static_cast<char*>(g_scratch_ptr[dev]);
+    out->counters = reinterpret_cast<unsigned*>(base);
+    out->n_counters = kScratchCounters;
+    out->partials = reinterpret_cast<float*>(base + kScratchCounterBytes);
+    out->partial_floats = kScratchPartialBytes / sizeof(float);
+    return TP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -166,28 +221,39 @@ tp_status_t tp_linear_row_partial(const void* X_r, int64_t ldx, const void* W_r,
 tp_status_t tp_mlp_shard(const void* X, const void* Wg_r, const void* Wu_r, const void* bg_r, const void* bu_r,
                          const void* Wd_r, void* H_r, void* P_r, int64_t M, int64_t hidden, int64_t intermediate,
                          int32_t tp_size, tp_dtype_t dtype, tp_dtype_t partial_dtype, void* stream) {
-    if (!X || !Wg_r || !Wu_r || !H_r) return TP_ERR_NULL;
-    if (P_r && !Wd_r) return TP_ERR_NULL;
-    if ((bg_r == nullptr) != (bu_r == nullptr)) return TP_ERR_NULL;
-    if (!dtype_ok(dtype) || !dtype_ok(partial_dtype)) return TP_ERR_DTYPE;
-    if (dtype == TP_DTYPE_F32 && partial_dtype != TP_DTYPE_F32) return TP_ERR_DTYPE;
-    TP_TRY(check_dims(M, {hidden, intermediate}));
-    if (tp_size < 1 || tp_size > kMaxTP) return TP_ERR_SHAPE;
-    if (intermediate % tp_size != 0) return TP_ERR_INDIVISIBLE;
-    const int64_t i = intermediate / tp_size;
-    TP_TRY(check_vec_operand(X, hidden, dtype));
-    TP_TRY(check_vec_operand(Wg_r, hidden, dtype));
-    TP_TRY(check_vec_operand(Wu_r, hidden, dtype));
-    if (P_r) {
-        TP_TRY(check_vec_operand(H_r, i, dtype));
-        TP_TRY(check_vec_operand(Wd_r, i, dtype));
-    }
-    const LinearDesc up{X, hidden, Wg_r, Wu_r, bg_r, bu_r, H_r, i, M, i, hidden, dtype, dtype, true};
-    const LinearDesc down{H_r, i, Wd_r, nullptr, nullptr, nullptr, P_r, hidden, M, hidden, i, dtype, partial_dtype, false};
+    LinearDesc up, down;
+    TP_TRY(mlp_descs(X, Wg_r, Wu_r, bg_r, bu_r, Wd_r, H_r, P_r, M, hidden, intermediate, tp_size, dtype,
+                     partial_dtype, &up, &down));
     return planned(static_cast<hipStream_t>(stream), [&](const Ctx& c) {
         TP_TRY(launch_linear(up, c));
         return P_r ? launch_linear(down, c) : TP_OK;
     });
+}
+
+tp_status_t tp_mlp_shard_noalloc(const void* X, const void* Wg_r, const void* Wu_r, const void* bg_r,
+                                 const void* bu_r, const void* Wd_r, void* H_r, void* P_r, int64_t M, int64_t hidden,
+                                 int64_t intermediate, int32_t tp_size, tp_dtype_t dtype, tp_dtype_t partial_dtype,
+                                 void* stream) {
+    LinearDesc up, down;
+    TP_TRY(mlp_descs(X, Wg_r, Wu_r, bg_r, bu_r, Wd_r, H_r, P_r, M, hidden, intermediate, tp_size, dtype,
+                     partial_dtype, &up, &down));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    auto body = [&](const Ctx& c) {
+        TP_TRY(launch_linear(up, c));
+        return P_r ? launch_linear(down, c) : TP_OK;
+    };
+    WsNeed need;
+    TP_TRY(body(Ctx{s, nullptr, &need}));
+    if (need.partial_floats * sizeof(float) > kScratchPartialBytes || need.counters > kScratchCounters)
+        return TP_ERR_WORKSPACE;
+    if (t_planning) return TP_OK;  // it needs no reserved work space
+    Workspace ws;
+    if (!need.empty()) {
+        TP_TRY(scratch_of_current_device(&ws));
+        // The array keeps the previous call's contents: the counters this call uses start at zero.
+        if (need.counters) TP_TRY(launch_fill_u32(ws.counters, need.counters, 0u, s));
+    }
+    return body(Ctx{s, &ws, nullptr});
 }
 
 tp_status_t tp_ffn_gelu_shard(const void* X, const void* W1_r, const void* b1_r, const void* W2_r, void* H_r,

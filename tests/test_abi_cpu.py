@@ -31,7 +31,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     for name in names:
         assert hasattr(L, name), name
     assert set(names) == set(tp.EXPORTS)
