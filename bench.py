@@ -168,11 +168,11 @@ class Layer:
             timed("down", lambda: tp.tp_linear_row_partial(sh["H"], self.i, sh["Wd"], sh["Pd"], M, self.inter,
                                                            h, p))
         timed("sum", lambda: tp.tp_combine_sum([sh["Pd"] for sh in self.shards], self.bd, self.Y, M, h))
-        timed("concat", lambda: tp.tp_combine_concat([sh["QKV"] for sh in self.shards], self.seg, self.QKVc, M))
-        timed("concat", lambda: tp.tp_combine_concat([sh["H"] for sh in self.shards], [self.i], self.Hc, M))
+        timed("concat_qkv", lambda: tp.tp_combine_concat([sh["QKV"] for sh in self.shards], self.seg, self.QKVc, M))
+        timed("concat_h", lambda: tp.tp_combine_concat([sh["H"] for sh in self.shards], [self.i], self.Hc, M))
 
 
-def attention_bench(layer, reps=5):
+def attention_bench(layer, reps=20):
     """The head-local attention core on each of the layer's 8 shards (its own QKV_r from the
     timed step: 8 query heads and 1 KV head of 128, causal over the 4096 tokens). Not part of
     the layer step above, whose attention stand-in is A := Q. Work per shard: 2 products of
@@ -267,7 +267,7 @@ def hold_gpu(seconds):
         pass
 
 
-def decode_bench(iters=30):
+def decode_bench(iters=100):
     import torch
     import tensor_transformer_linear_col_amd as tp
     import tp_inputs as I
@@ -409,7 +409,84 @@ def _median_launch_us(fn, n_sets, iters):
     return sorted(a.elapsed_time(b) for a, b in evs)[len(evs) // 2] * 1e3
 
 
-def split_variants_bench(iters=30):
+def _back_to_back_us(fn, n_sets, iters):
+    """The same launches back to back between one pair of events (the rate of a stream of
+    such kernels), weights still rotated."""
+    import torch
+    hold_gpu(5e-3)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for it in range(iters):
+        fn(it % n_sets)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / iters
+
+
+def attnproj_bench(iters=100):
+    """The 70B attention-projection shard at TP = 8 (64 query / 8 KV heads of 128, hidden
+    8192): the QKV column product 8192 -> 1280 (8 Q heads, 1 K, 1 V) and the O row partial
+    1024 -> 8192. At one token (decode, HBM-bound) the weights rotate through > 1 GiB of
+    copies so the 256 MB Infinity Cache cannot serve them; at 2048 tokens (prefill,
+    MFMA-bound) the 8 shards' weights are taken in turn. Algorithmic bytes: weights + X +
+    output; flops: 2 M N K."""
+    import torch
+    import tensor_transformer_linear_col_amd as tp
+    import tp_inputs as I
+    BF = torch.bfloat16
+    shape = I.LLAMA70B_ATTN_TP8
+    h, nh, nkv, d, p = shape.hidden, shape.n_heads, shape.n_kv_heads, shape.head_dim, shape.tp
+    nq, ka = (nh // p + 2 * nkv // p) * d, nh // p * d
+    wt = I.attn_weights(shape, with_bias=False)
+    Wqkv, Wo = wt["Wqkv"].cuda(), wt["Wo"].cuda()
+    base = []
+    for r in range(p):
+        wq = torch.empty(nq, h, dtype=BF, device="cuda")
+        wo = torch.empty(h, ka, dtype=BF, device="cuda")
+        tp.tp_shard_qkv(Wqkv, h, nh, nkv, d, p, r, wq)
+        tp.tp_shard_weight(Wo, h, nh * d, p, r, 1, wo)
+        base.append((wq, wo))
+    del Wqkv, Wo, wt
+    shard_bytes = (nq * h + h * ka) * 2
+    copies = max(p, -(-(1 << 30) // shard_bytes) + 1)
+    sets = base + [tuple(t.clone() for t in base[c % p]) for c in range(p, copies)]
+    out = []
+    for M in shape.tokens:
+        x = I.activations(M, h, I.activation_seed(shape.seed, M)).cuda()
+        a = I.activations(M, ka, I.activation_seed(shape.seed, M, slot=1)).cuda()
+        QKV = torch.empty(M, nq, dtype=BF, device="cuda")
+        P = torch.empty(M, h, dtype=BF, device="cuda")
+        qkv_fn = lambda c: tp.tp_attn_proj_shard(x, sets[c][0], None, QKV, None, None, None, M, h, nh, nkv, d, p)
+        o_fn = lambda c: tp.tp_attn_proj_shard(None, None, None, None, a, sets[c][1], P, M, h, nh, nkv, d, p)
+        reserve_for(lambda: (qkv_fn(0), o_fn(0)))
+        n_sets = len(sets) if M <= 64 else p
+        for c in range(n_sets):  # warm
+            qkv_fn(c)
+            o_fn(c)
+        torch.cuda.synchronize()
+        n_it = iters if M <= 64 else max(16, iters // 4)
+        for op, fn, by, fl in (("qkv_col", qkv_fn, nq * h * 2 + M * h * 2 + M * nq * 2, 2.0 * M * nq * h),
+                               ("o_row_partial", o_fn, h * ka * 2 + M * ka * 2 + M * h * 2, 2.0 * M * h * ka)):
+            us = _median_launch_us(fn, n_sets, n_it)
+            us_b2b = _back_to_back_us(fn, n_sets, n_it)
+            rec = {"workload": shape.name, "M": M, "op": op, "us": round(us, 2), "us_back_to_back": round(us_b2b, 2),
+                   "GB_s": round(by / us / 1e3, 1), "TFLOP_s": round(fl / us / 1e6, 2)}
+            if M <= 64:
+                rec["kernel"] = "skinny_kernel"
+                rec["hbm_frac"] = round(by / us / 1e3 / HBM_PEAK_GBS, 3)
+                rec["hbm_frac_back_to_back"] = round(by / us_b2b / 1e3 / HBM_PEAK_GBS, 3)
+            else:
+                rec["kernel"] = "gemm_dtl_kernel" + (" + splitk_reduce_kernel" if op == "qkv_col" else "")
+                rec["bf16_frac"] = round(fl / us / 1e6 / BF16_PEAK_TFLOPS, 4)
+                rec["bf16_frac_back_to_back"] = round(fl / us_b2b / 1e6 / BF16_PEAK_TFLOPS, 4)
+            out.append(rec)
+            log(f"attention projection {shape.name} M={M} {op}: {us:.1f} us per launch, {us_b2b:.1f} us back to back")
+    del sets, base
+    torch.cuda.empty_cache()
+    return out
+
+
+def split_variants_bench(iters=100):
     """Decode shards of the two split variants: an uneven column split (the 7B FFN's 11008
     gate rows over 3 shards, 3672 + 3672 + 3664, which the listing's divisibility assert would
     reject) and a QKV shard with KV-head replication (70B attention at TP = 16: 4 Q heads and
@@ -469,11 +546,14 @@ def cpu_baseline(shape, target_s):
     import numpy as np
     import oracle as O
     import tp_inputs as I
+    host_cores = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
+        blas = [d for d in threadpool_info() if d.get("user_api") == "blas"]
+        threads = max([d.get("num_threads", 1) for d in blas] or [1])
+        backend = ", ".join(sorted({f"{d.get('internal_api')} {d.get('version')}" for d in blas})) or "unknown"
     except Exception:
-        threads = os.cpu_count() or 1
+        threads, backend = host_cores, "unknown"
     aw = I.attn_weights(shape, with_bias=True)
     fw = I.ffn_weights(shape, with_bias=True)
     w = {k: I.as_numpy_f64(v) for k, v in {**aw, **fw}.items()}
@@ -493,6 +573,7 @@ def cpu_baseline(shape, target_s):
         S = int(min(M, max(2 * S, S * target_s / max(dt, 1e-3))))
     tflops = S * flop_per_token / dt / 1e12
     return {"value": round(tflops, 4), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "host_cores_available": host_cores, "blas_backend": backend, "blas_threads": int(threads),
             "sample": f"{S} of {M} tokens through the unsharded fp64 layer chain (numpy float64 BLAS), "
                       f"{dt:.1f} s"}
 
@@ -520,7 +601,8 @@ def main():
     import tp_inputs as I
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.decode_only:
-        print(json.dumps({"decode": decode_bench(), "attention_decode": attention_decode_bench()}), flush=True)
+        print(json.dumps({"decode": decode_bench(), "attention_projection": attnproj_bench(),
+                          "attention_decode": attention_decode_bench()}), flush=True)
         return
     if args.traffic_copy_mib > 0:
         # A plain copy of known size: reads and writes exactly n bytes each. Under
@@ -574,11 +656,15 @@ def main():
     sum_bytes = (layer.p + 1) * M * h * 2 + h * 2
     kernels["combine_sum"] = {"us_per_launch": round(per["sum"] * 1e3, 1),
                               "GB_s": round(sum_bytes / (per["sum"] * 1e-3) / 1e9, 1)}
-    kernels["combine_concat"] = {"us_per_launch": round(per["concat"] * 1e3, 1)}
+    for name, width in (("concat_qkv", layer.QKVc.shape[1]), ("concat_h", layer.Hc.shape[1])):
+        by = 2 * M * width * 2  # every element read once and written once
+        kernels[f"combine_{name}"] = {"us_per_launch": round(per[name] * 1e3, 1),
+                                      "GB_s": round(by / (per[name] * 1e-3) / 1e9, 1)}
 
     attention = attention_bench(layer)
     decode = None if args.skip_decode else decode_bench()
     attention_decode = None if args.skip_decode else attention_decode_bench()
+    attention_projection = None if args.skip_decode else attnproj_bench()
     cpu = None if args.skip_cpu_baseline else cpu_baseline(shape, args.cpu_seconds)
 
     out = {
@@ -605,6 +691,7 @@ def main():
         "kernels": kernels,
         "attention_core": attention,
         "decode": decode,
+        "attention_projection": attention_projection,
         "attention_decode": attention_decode,
         "cpu_baseline": cpu,
     }

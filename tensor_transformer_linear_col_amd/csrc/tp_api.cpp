@@ -32,11 +32,6 @@ tp_status_t check_dims(int64_t M, std::initializer_list<int64_t> pos) {
     return TP_OK;
 }
 
-#define TP_TRY(expr)                       \
-    do {                                   \
-        const tp_status_t st_ = (expr);    \
-        if (st_ != TP_OK) return st_;      \
-    } while (0)
 
 tp_status_t launch_linear(const LinearDesc& d, const Ctx& c) {
     if (d.M == 0) return TP_OK;

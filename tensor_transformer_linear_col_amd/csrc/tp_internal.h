@@ -86,6 +86,12 @@ tp_status_t launch_copy2d(const void* src, int64_t lds, void* dst, int64_t ldd, 
                           int64_t cols, size_t elem, hipStream_t stream);
 tp_status_t launch_fill_u32(unsigned* p, size_t n, unsigned v, hipStream_t stream);
 
+#define TP_TRY(expr)                    \
+    do {                                \
+        const tp_status_t st_ = (expr); \
+        if (st_ != TP_OK) return st_;   \
+    } while (0)
+
 inline tp_status_t hip_status() {
     return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_HIP;
 }
