@@ -179,8 +179,10 @@ tp_status_t tp_attn_proj_shard(const void* X, const void* Wqkv_r, const void* bq
  * tp_attn_proj_shard writes them; hq = n_heads/p, hk = KV heads per shard, replicated as
  * for tp_shard_qkv). A_r : [M, hq*d], the input tp_attn_proj_shard's O half expects.
  * bf16 only (TP_ERR_DTYPE otherwise); head_dim 64 or 128 (TP_ERR_SHAPE otherwise);
- * TP_ERR_INDIVISIBLE if the heads do not split or group evenly. fp32 softmax and
- * accumulation, one rounding. */
+ * TP_ERR_INDIVISIBLE if the heads do not split or group evenly. Scores, the softmax and the
+ * accumulation are fp32; each softmax weight is rounded to bf16 where it enters the P*V
+ * product on the matrix cores (whose operands are bf16), the normaliser sums the fp32
+ * weights, and each output is rounded once to bf16. */
 tp_status_t tp_attn_core_shard(const void* QKV_r, void* A_r, int64_t M, int32_t n_heads,
                                int32_t n_kv_heads, int32_t head_dim, int32_t tp_size,
                                int32_t causal, tp_dtype_t dtype, void* stream);

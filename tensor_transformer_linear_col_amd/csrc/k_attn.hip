@@ -34,7 +34,9 @@
 //       16-byte read per lane.
 // The causal mask and the sequence-end mask are applied only on blocks that need them.
 // O^T registers hold one query per lane, so the rescale, the merge and the final 1/l
-// are per-lane scalars. Softmax and accumulation are fp32; A_r is rounded once to bf16.
+// are per-lane scalars. Softmax and accumulation are fp32; each weight P is rounded to
+// bf16 where it becomes the P*V product's MFMA operand (the normaliser l sums the fp32
+// weights), and A_r is rounded once to bf16.
 #include <algorithm>
 #include <vector>
 #include <type_traits>
@@ -460,7 +462,8 @@ constexpr int kWQ = 4;  // query slices per workgroup: 128 query rows, 8 waves
 // head, row); thread (j, d4) takes the ranges q = j, j + 8, ... (independent loads, all in
 // flight at once) for 4 consecutive d, merging them online in that order; the 8 partial
 // results then meet through LDS in j order. Fixed order throughout, one division by the
-// merged sum, one rounding.
+// merged sum, and the output rounded once to bf16 (the ranges' weights were rounded to bf16
+// where they entered their P*V products).
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p, int nqb) {
     constexpr int QB = 32 * kWQ, NJ = 256 / (D / 4);  // range lanes: 8 (D = 128) or 16 (D = 64)

@@ -1,8 +1,8 @@
 // Decode-shaped shard GEMM (M <= 64 tokens): Y = X W^T (+ b), or the SwiGLU pair.
 //
 // At decode sizes the product is bound by streaming the weight shard from HBM
-// ("What is tensor parallelism?", section "Why it helps when serving": every GPU
-// reads its own slice of the weights). The kernel therefore:
+// ("What is tensor parallelism?", section "Why it helps when serving": each GPU's
+// weight traffic is only its own shard). The kernel therefore:
 //   * reads every weight byte exactly once with 16-byte loads, keeping several
 //     loads per lane in flight (register ping-pong between K chunks);
 //   * does the multiply on MFMA (v_mfma_f32_16x16x32_bf16): the weight tile is the
@@ -32,24 +32,15 @@
 
 #include "tp_epilogue.h"
 
-#ifndef TP_SKINNY_WG_PER_CU
-#define TP_SKINNY_WG_PER_CU 1
-#endif
-#ifndef TP_SKINNY_U1
-#define TP_SKINNY_U1 4
-#endif
-#ifndef TP_SKINNY_U4
-#define TP_SKINNY_U4 2
-#endif
-#ifndef TP_SKINNY_M2
-#define TP_SKINNY_M2 5
-#endif
-#ifndef TP_SKINNY_M4G
-#define TP_SKINNY_M4G 3
-#endif
-
 namespace tp {
 namespace {
+
+// Tile choices, each measured on the decode shards (70B TP=4, 7B TP=2):
+constexpr int kWgPerCu = 1;    // split-K grid target: workgroups per CU
+constexpr int kU1 = 4;         // 32-wide K steps per piece, one token tile, plain products
+constexpr int kU4 = 2;         // 32-wide K steps per piece, four token tiles
+constexpr int kTwoRowsM = 5;   // from this many tokens, two row tiles per wave (plain)
+constexpr int kPairTilesM = 3; // from this many tokens, 2 gate + 2 up tiles per wave (SwiGLU)
 
 struct SkinnyParams {
     const bf16* X;
@@ -341,7 +332,7 @@ tp_status_t run(const LinearDesc& d, const Ctx& c, bool whole_k = false) {
         C = ceil_div(d.K, CK);
         P = std::min<int64_t>(G * C, (int64_t)device_cus());
     } else {
-        const int64_t target = TP_SKINNY_WG_PER_CU * (int64_t)device_cus();
+        const int64_t target = kWgPerCu * (int64_t)device_cus();
         int64_t S = whole_k ? 1 : ceil_div(target, G);
         const int64_t smax = std::max<int64_t>(1, d.K / (NW * KS));
         S = std::min<int64_t>(std::max<int64_t>(S, 1), std::min<int64_t>(smax, 64));
@@ -389,19 +380,19 @@ tp_status_t launch_skinny(const LinearDesc& d, const Ctx& c) {
     if (d.swiglu) {
         switch (mt) {
             case 1:
-                // From TP_SKINNY_M4G tokens on, two gate and two up tiles per wave halve the token
+                // From kPairTilesM tokens on, two gate and two up tiles per wave halve the token
                 // reloads, which then cost more than the shorter weight stream per wave. Only
                 // where those 32-output row groups by themselves occupy at least 80% of the CUs:
                 // K is then not split, as the cross-workgroup reduction of a split costs more
                 // than the reloads saved (measured on the 70B and 7B FFN shards).
-                if (d.M >= TP_SKINNY_M4G && ceil_div(d.N, 32) * 5 >= (int64_t)device_cus() * 4)
+                if (d.M >= kPairTilesM && ceil_div(d.N, 32) * 5 >= (int64_t)device_cus() * 4)
                     return run_bias<1, 4, 8, 2, false, kActSwiglu>(d, c, true);
                 // A long weight stream (>= 640 KB per CU) is dealt in equal ranges, one workgroup
                 // per CU: one workgroup per row group leaves some CUs two row groups and others
                 // one (measured: 70B TP=4 at 1 token 51.4 -> 48 us; the 7B TP=2 shard, 352 KB per
                 // CU, is faster with one workgroup per row group).
                 if (4 * d.N * d.K >= (int64_t)device_cus() * (640 << 10))
-                    return run_bias<1, 2, 8, TP_SKINNY_U1, true, kActSwiglu>(d, c);
+                    return run_bias<1, 2, 8, kU1, true, kActSwiglu>(d, c);
                 // Shorter streams: two 32-wide K steps per piece (measured: 7B TP=2 gate/up at 1
                 // token 25.2 -> 24.2 us; four steps stay best for the plain products).
                 return run_bias<1, 2, 8, 2, false, kActSwiglu>(d, c);
@@ -411,8 +402,8 @@ tp_status_t launch_skinny(const LinearDesc& d, const Ctx& c) {
                 return run_bias<2, 2, 4, 2, false, kActSwiglu>(d, c);
             case 3:  // three token tiles run as four: 1 + 1 tiles per wave reload tokens more than the
                      // padded rows cost (measured: 70B TP=4 at 48 tokens 79 -> 63 us, 7B TP=2 42 -> 35 us)
-                return run_bias<4, 4, 4, TP_SKINNY_U4, true, kActSwiglu>(d, c);
-            case 4: return run_bias<4, 4, 4, TP_SKINNY_U4, true, kActSwiglu>(d, c);
+                return run_bias<4, 4, 4, kU4, true, kActSwiglu>(d, c);
+            case 4: return run_bias<4, 4, 4, kU4, true, kActSwiglu>(d, c);
             default: return TP_ERR_SHAPE;
         }
     }
@@ -420,13 +411,13 @@ tp_status_t launch_skinny(const LinearDesc& d, const Ctx& c) {
         constexpr int A = decltype(act)::value;
         switch (mt) {
             case 1:
-                // From TP_SKINNY_M2 tokens on, two row tiles per token load halve the token
+                // From kTwoRowsM tokens on, two row tiles per token load halve the token
                 // reloads (measured: 70B TP=4 down at 16 tokens 34 -> 26 us).
-                if (d.M >= TP_SKINNY_M2) return run_bias<1, 2, 8, 2, false, A>(d, c);
-                return run_bias<1, 1, 8, TP_SKINNY_U1, false, A>(d, c);
+                if (d.M >= kTwoRowsM) return run_bias<1, 2, 8, 2, false, A>(d, c);
+                return run_bias<1, 1, 8, kU1, false, A>(d, c);
             case 2: return run_bias<2, 2, 4, 2, false, A>(d, c);
             case 3: return run_bias<3, 2, 4, 2, false, A>(d, c);
-            case 4: return run_bias<4, 4, 4, TP_SKINNY_U4, true, A>(d, c);
+            case 4: return run_bias<4, 4, 4, kU4, true, A>(d, c);
             default: return TP_ERR_SHAPE;
         }
     };

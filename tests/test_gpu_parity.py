@@ -37,7 +37,7 @@ def test_toy_column_split_concat_fp32():
     assert err(Y, ref) <= F32_TOL
     printed = [float(v) for v in read_golden("toy_tp2.txt")["combined_output_round4"]]
     np.testing.assert_array_equal(np.round(host64(Y)[0], 4), printed)
-    assert W_r.numel() == 24   # "GPU 0 held 24 of 48 weight values"
+    assert W_r.numel() == 24   # the printed output's weight count of one shard: 24 of the 48
 
 
 def test_toy_row_split_sum_fp32():
