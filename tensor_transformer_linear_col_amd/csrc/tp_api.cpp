@@ -36,6 +36,11 @@ tp_status_t check_dims(int64_t M, std::initializer_list<int64_t> pos) {
 tp_status_t launch_linear(const LinearDesc& d, const Ctx& c) {
     if (d.M == 0) return TP_OK;
     if (d.in_dtype == TP_DTYPE_F32) return launch_f32(d, c);
+    // 1-4 tokens with fewer 16-feature row groups than CUs: the MFMA decode kernel would cut
+    // K across workgroups (a partial-sum hand-off of several memory round trips at the end);
+    // the GEMV kernel splits the features one by one instead (70B QKV shard at TP=8 and one
+    // token: 10.3 -> 8.4 us). With enough row groups the MFMA kernel stays faster.
+    if (d.M <= 4 && gemv_chunks(d.K, nullptr) != 0 && ceil_div(d.N, 16) < gemv_cus()) return launch_gemv(d, c);
     if (d.M <= 64) return launch_skinny(d, c);
     return launch_gemm(d, c);
 }

@@ -66,6 +66,13 @@ struct Ctx {
 
 // Kernel launchers (the C ABI layer has validated the arguments).
 tp_status_t launch_skinny(const LinearDesc& d, const Ctx& c);
+// 1-4 tokens: one workgroup per CU over balanced feature ranges, no cross-workgroup sums.
+tp_status_t launch_gemv(const LinearDesc& d, const Ctx& c);
+// 512-wide K chunks per wave of launch_gemv for K (1, 2 or 4; 0 when K is too long for it),
+// and the K elements per wave.
+int gemv_chunks(int64_t K, int* kw_out);
+// Compute units of the current device (256 when it cannot be read).
+int gemv_cus();
 tp_status_t launch_gemm(const LinearDesc& d, const Ctx& c);
 tp_status_t launch_f32(const LinearDesc& d, const Ctx& c);
 // Head-local attention core: out[M, hq*d] (row stride lda) from qkv[M, (hq+2hk)*d] (row stride ldq).

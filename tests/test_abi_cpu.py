@@ -240,17 +240,21 @@ def test_dry_run_sizes_the_split_reductions(L):
     # cut into 3 K ranges -> 240 fp32 partial tiles of 256 KB.
     qkv = lambda: L.tp_attn_proj_shard(P, P, 0, P, 0, 0, 0, 4096, 8192, 64, 8, 128, 8, BF16, BF16, None)
     assert _plan(L, qkv) == (OK, 240 * 256 * 256 * 4, 0)
-    # The same QKV shard at one token: 80 row groups of 16 outputs, K cut in 4 -> 320
-    # workgroups with two 1 KB partial tiles each, and one arrival counter per row group.
-    qkv1 = lambda: L.tp_attn_proj_shard(P, P, 0, P, 0, 0, 0, 1, 8192, 64, 8, 128, 8, BF16, BF16, None)
-    assert _plan(L, qkv1) == (OK, 320 * 2 * 256 * 4, 80)
+    # The same QKV shard at 8 tokens: 40 row groups of 32 outputs, K cut in 7 -> 280
+    # workgroups with two 2 KB partial tiles each, and one arrival counter per row group.
+    qkv1 = lambda: L.tp_attn_proj_shard(P, P, 0, P, 0, 0, 0, 8, 8192, 64, 8, 128, 8, BF16, BF16, None)
+    assert _plan(L, qkv1) == (OK, 280 * 2 * 512 * 4, 40)
+    # At 1 to 4 tokens the GEMV kernel splits the features across workgroups, not K.
+    for m in (1, 4):
+        assert _plan(L, lambda: L.tp_attn_proj_shard(P, P, 0, P, 0, 0, 0, m, 8192, 64, 8, 128, 8, BF16, BF16,
+                                                     None)) == (OK, 0, 0)
     # Products that split nothing need no work space; M = 0 does nothing at all.
     gateup = lambda: L.tp_mlp_shard(P, P, P, 0, 0, P, P, P, 4096, 8192, 28672, 8, BF16, BF16, None)
     assert _plan(L, gateup) == (OK, 0, 0)
     assert _plan(L, lambda: col(L, M=0)) == (OK, 0, 0)
     # Several calls: the largest need of any of them.
     both = lambda: (qkv1(), qkv(), gateup())[-1]
-    assert _plan(L, both) == (OK, 240 * 256 * 256 * 4, 80)
+    assert _plan(L, both) == (OK, 240 * 256 * 256 * 4, 40)
     # Validation still applies inside a dry run.
     assert _plan(L, lambda: col(L, X=0))[0] == NULL
 

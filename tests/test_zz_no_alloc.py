@@ -35,8 +35,8 @@ def _run(fn, X, w, M, hidden, inter, p, i):
 
 
 # (M, hidden, intermediate, tp): the 7B FFN shard at 8 tokens (its down product cuts K across
-# workgroups), then a smaller shard at 4 tokens (its gate/up product cuts K).
-CALLS = [(8, 4096, 11008, 2), (4, 1024, 2816, 4)]
+# workgroups), then a smaller shard at 6 tokens (its gate/up product cuts K).
+CALLS = [(8, 4096, 11008, 2), (6, 1024, 2816, 4)]
 
 
 def test_noalloc_matches_the_reserved_entry_point_on_two_calls():
