@@ -43,6 +43,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time")
     ap.add_argument("--traffic-copy-mib", type=int, default=0,
                     help="first run one plain contiguous copy of this many MiB (counter calibration)")
+    ap.add_argument("--traffic-dma-check", action="store_true",
+                    help="then one LDS-DMA GEMM whose every weight byte is read once (256 tokens x 65536 x 1024: "
+                         "128 MiB of weights read, 32 MiB written), to check the calibration on DMA loads")
+    ap.add_argument("--decode-iters", type=int, default=100, help="launches per decode measurement")
     return ap.parse_args()
 
 
@@ -129,15 +133,29 @@ class Layer:
             "down": 2.0 * M * h * self.i * p,
         }
         self.total_flops = sum(self.flops.values())
+        # The two concats only check the split; they run on a second stream (default
+        # priority) and overlap the GEMMs that follow their inputs.
+        self.side = torch.cuda.Stream()
         need = reserve_for(lambda: (self.step(), self.step(core=True)))
         log(f"work space: {need.partial_bytes / 2**20:.1f} MiB of partials, {need.n_counters} counters")
 
     def step(self, ev=None, core=False, only=None):
         """One pass of the shard path. ev: optional dict name -> list of (start, end) events,
         recorded around the launches named in `only` (all when None). core: run the head-local
-        attention core between QKV and O instead of A := Q."""
+        attention core between QKV and O instead of A := Q. The concats run on the side stream
+        (each after its inputs are written, the step ending when both are done), except when
+        every launch is timed, where they stay on the main stream to be timed too."""
         tp, torch = self.tp, self.torch
         M, h, p = self.M, self.h, self.p
+        overlap = not (ev is not None and only is None)
+        main = torch.cuda.current_stream()
+
+        def on_side(fn):
+            done = torch.cuda.Event()
+            done.record(main)
+            self.side.wait_event(done)
+            with torch.cuda.stream(self.side):
+                fn()
 
         def timed(name, fn):
             if ev is None or (only is not None and name not in only):
@@ -161,15 +179,24 @@ class Layer:
             # A := Q: the shard's Q heads are the first ka columns of QKV_r (row stride nq)
             timed("o", lambda: tp.tp_linear_row_partial(sh["QKV"], self.nq, sh["Wo"], sh["Po"], M,
                                                         self.nh * self.d, h, p))
+        concat_qkv = lambda: tp.tp_combine_concat([sh["QKV"] for sh in self.shards], self.seg, self.QKVc, M)
+        concat_h = lambda: tp.tp_combine_concat([sh["H"] for sh in self.shards], [self.i], self.Hc, M)
+        if overlap:
+            on_side(concat_qkv)
         timed("sum", lambda: tp.tp_combine_sum([sh["Po"] for sh in self.shards], self.bo, self.Y1, M, h))
-        for sh in self.shards:
+        for r, sh in enumerate(self.shards):
             timed("gateup", lambda: tp.tp_mlp_shard(self.Y1, sh["Wg"], sh["Wu"], sh["bg"], sh["bu"], None,
                                                     sh["H"], None, M, h, self.inter, p))
+            if overlap and r == p - 1:
+                on_side(concat_h)
             timed("down", lambda: tp.tp_linear_row_partial(sh["H"], self.i, sh["Wd"], sh["Pd"], M, self.inter,
                                                            h, p))
         timed("sum", lambda: tp.tp_combine_sum([sh["Pd"] for sh in self.shards], self.bd, self.Y, M, h))
-        timed("concat_qkv", lambda: tp.tp_combine_concat([sh["QKV"] for sh in self.shards], self.seg, self.QKVc, M))
-        timed("concat_h", lambda: tp.tp_combine_concat([sh["H"] for sh in self.shards], [self.i], self.Hc, M))
+        if overlap:
+            main.wait_stream(self.side)
+        else:
+            timed("concat_qkv", concat_qkv)
+            timed("concat_h", concat_h)
 
 
 def attention_bench(layer, reps=20):
@@ -409,6 +436,32 @@ def _median_launch_us(fn, n_sets, iters):
     return sorted(a.elapsed_time(b) for a, b in evs)[len(evs) // 2] * 1e3
 
 
+def stream_reference_bench(iters=60):
+    """A plain device copy (torch's copy kernel, one read and one write of every byte) at the
+    byte sizes of the decode shards, sources rotated through > 1 GiB: how close a kernel with
+    no arithmetic comes to the HBM rate at each size, i.e. the fixed cost of launching,
+    ramping up and draining a short stream on this chip."""
+    import torch
+    out = []
+    for mb in (16.8, 21.0, 45.1, 90.2, 117.4, 234.9):
+        n = int(mb * 1e6) // 2 // 8 * 8
+        copies = max(2, -(-(1 << 30) // (2 * n)) + 1)
+        srcs = [torch.empty(n, dtype=torch.bfloat16, device="cuda").fill_(1.0) for _ in range(copies)]
+        dst = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+        fn = lambda c: dst.copy_(srcs[c])
+        for c in range(copies):
+            fn(c)
+        torch.cuda.synchronize()
+        us = _back_to_back_us(fn, copies, iters)
+        gbs = 2 * n * 2 / us / 1e3
+        out.append({"MB_read": round(2 * n / 1e6, 1), "us_back_to_back": round(us, 2), "GB_s_read_plus_write": round(gbs, 1),
+                    "hbm_frac": round(gbs / HBM_PEAK_GBS, 3)})
+        del srcs, dst
+    torch.cuda.empty_cache()
+    log("plain copy reference: " + ", ".join(f"{r['MB_read']} MB {r['hbm_frac']}" for r in out))
+    return {"kernel": "torch copy_ (read + write)", "sizes": out}
+
+
 def _back_to_back_us(fn, n_sets, iters):
     """The same launches back to back between one pair of events (the rate of a stream of
     such kernels), weights still rotated."""
@@ -601,8 +654,9 @@ def main():
     import tp_inputs as I
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.decode_only:
-        print(json.dumps({"decode": decode_bench(), "attention_projection": attnproj_bench(),
-                          "attention_decode": attention_decode_bench()}), flush=True)
+        print(json.dumps({"decode": decode_bench(args.decode_iters), "attention_projection": attnproj_bench(args.decode_iters),
+                          "attention_decode": attention_decode_bench(),
+                          "stream_reference": stream_reference_bench()}), flush=True)
         return
     if args.traffic_copy_mib > 0:
         # A plain copy of known size: reads and writes exactly n bytes each. Under
@@ -615,6 +669,14 @@ def main():
         tp.tp_shard_weight(src, rows, cols, 1, 0, 0, dst)
         torch.cuda.synchronize()
         del src, dst
+        if args.traffic_dma_check:
+            M, N, K = 256, 65536, 1024  # 256 tiles of 256 x 256 on the LDS-DMA kernel, one per CU
+            x = torch.ones(M, K, dtype=torch.bfloat16, device="cuda")
+            w = torch.ones(N, K, dtype=torch.bfloat16, device="cuda")
+            y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+            tp.tp_linear_col(x, w, None, y, M, K, N, 1)
+            torch.cuda.synchronize()
+            del x, w, y
     shape = I.LLAMA70B_LAYER_TP8
     layer = Layer(shape)
 
@@ -662,9 +724,10 @@ def main():
                                       "GB_s": round(by / (per[name] * 1e-3) / 1e9, 1)}
 
     attention = attention_bench(layer)
-    decode = None if args.skip_decode else decode_bench()
+    decode = None if args.skip_decode else decode_bench(args.decode_iters)
     attention_decode = None if args.skip_decode else attention_decode_bench()
-    attention_projection = None if args.skip_decode else attnproj_bench()
+    attention_projection = None if args.skip_decode else attnproj_bench(args.decode_iters)
+    stream_reference = None if args.skip_decode else stream_reference_bench()
     cpu = None if args.skip_cpu_baseline else cpu_baseline(shape, args.cpu_seconds)
 
     out = {
@@ -693,6 +756,7 @@ def main():
         "decode": decode,
         "attention_projection": attention_projection,
         "attention_decode": attention_decode,
+        "stream_reference": stream_reference,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
