@@ -15,9 +15,12 @@
 // the block), each with its own running maximum, sum and output accumulators; the two
 // halves are merged once at the end. Two waves per SIMD let one wave's softmax run
 // while the other's MFMAs do. Keys and values stream through LDS 64 at a time,
-// double-buffered: the next block is fetched into registers while the current one is
-// used and written to the other LDS buffer afterwards, so one barrier per block
-// suffices; all eight waves share each block. Per block and wave:
+// double-buffered, by DMA (buffer loads that write LDS directly, no registers): the next
+// block is requested into the other buffer right after the barrier that frees it and
+// lands while the current one is used, so one barrier per block suffices; all eight
+// waves share each block. K and V rows sit in LDS as loaded (one row per key), their
+// 16-byte chunks XOR-swizzled by row so that the fragment reads below hit distinct
+// banks. Per block and wave:
 //   S^T = K Q^T on MFMA 32x32x16 bf16 (A = the wave's 32 keys from LDS, B = its 32
 //       queries, held in registers for the whole loop), so each lane holds 16 scores of
 //       one query: register e <-> key 8*(e/4) + 4*lh + e%4 of the half (lh = lane / 32);
@@ -29,9 +32,13 @@
 //   O^T += V^T P^T on MFMA, P^T straight from the score registers as the B operand.
 //       An MFMA reduces its 16 K positions in any order, so B holds a lane's keys as
 //       they come: lane half lh, step s: keys 16s + 4lh + {0..3}, then
-//       16s + 8 + 4lh + {0..3}. V^T is stored transposed in LDS with the keys of each
-//       16-key run in that order (4-key groups 0, 2, 1, 3), so the A operand is one
-//       16-byte read per lane.
+//       16s + 8 + 4lh + {0..3}. The A operand (one head-dim row of V^T per lane, those
+//       8 keys) comes from V's key rows through gfx950's LDS transpose read: within
+//       each 16-lane group, output lane 4a + b receives element b of the 8 bytes read
+//       by lanes a, a + 4, a + 8 and a + 12. With source lane 4r + a pointing at key
+//       r of a 4-key run, head-dim columns 4a .. 4a + 3 of a 16-column group, output
+//       lane i gets column i of the group across the 4 keys; two such reads per
+//       fragment give the 8 keys above.
 // The causal mask and the sequence-end mask are applied only on blocks that need them.
 // O^T registers hold one query per lane, so the rescale, the merge and the final 1/l
 // are per-lane scalars. Softmax and accumulation are fp32; each weight P is rounded to
@@ -81,20 +88,6 @@ struct AttnParams {
 
 constexpr int KB = 64;  // keys per block
 
-// 16 bytes at byte offset off of a raw buffer descriptor over [base, base + bytes): a lane
-// whose offset lies past the end reads zeros instead of touching memory (the bound check
-// covers the per-lane offset, so the whole offset is passed there). The descriptor type
-// exists only for the GPU target, so the body is compiled in the device pass alone.
-__device__ __forceinline__ bf16x8 load16(const void* base, uint32_t bytes, uint32_t off) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    const __amdgpu_buffer_rsrc_t rsrc =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0));
-#else
-    return bf16x8{};
-#endif
-}
-
 // Max and sum of a value over the two lane halves that hold one query (lanes i and i ^ 32):
 // one cross-half swap of the register (lanes 0..31 then hold the upper half's values and
 // the others the lower half's) instead of an LDS permute. Both halves get the same bits.
@@ -107,32 +100,42 @@ __device__ __forceinline__ float halves_sum(float v) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Storage position of key k of a block in the transposed V tile (see above).
-__device__ __forceinline__ int vpos(int k) {
-    const int g = (k >> 2) & 3;
-    return (k & ~15) | ((((g & 1) << 1) | (g >> 1)) << 2) | (k & 3);
+// 8 bytes from LDS through the transpose read (see the header).
+__device__ __forceinline__ bf16x4 ld_tr(const char* a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                          (__attribute__((address_space(3))) v4i16*)(const_cast<char*>(a))));
+#else
+    return bf16x4{};
+#endif
 }
+
+// s_waitcnt immediate: vmcnt(n) (n < 16) and lgkmcnt(0).
+constexpr unsigned kLgkm0Vm(int n) { return (unsigned)(n | (0x7 << 4)); }
 
 template <int D, bool CAUSAL, bool PACK, int WQ>
 __global__ __launch_bounds__(128 * WQ, 2) void attn_kernel(AttnParams p) {
     static_assert(D == 64 || D == 128, "head_dim 64 or 128");
     constexpr int QB = 32 * WQ;            // query rows per workgroup
     constexpr int NT = 128 * WQ;           // threads: WQ query slices x 2 key halves
-    constexpr int KP = D * 2 + 16;         // K tile row pitch (bytes): 16-byte pad
-    constexpr int VP = KB * 2 + 16;        // V^T tile row pitch (bytes): 16-byte pad
-    constexpr int KT = KB * KP;            // K tile bytes
-    constexpr int STG = KT + D * VP;       // one buffer: K tile, then V^T tile
+    constexpr int ROWB = D * 2;            // bytes per K or V row in LDS
+    constexpr int CPR = D / 8;             // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;          // rows per DMA instruction (64 lanes x 16 bytes)
+    constexpr int TILE = KB * ROWB;        // K or V tile bytes
+    constexpr int STG = 2 * TILE;          // one buffer: K tile, then V tile
     constexpr int NC = D / 16;             // 16-wide d chunks (MFMA K steps of S)
     constexpr int NB = D / 32;             // 32-row d blocks of O^T
-    constexpr int CK = KB * D / 8 / NT;    // 16-byte chunks of K per thread per block (2 or 1)
-    constexpr int R = CK;                  // keys per thread in the V transpose
-    constexpr int NKG = KB / R;            // key groups of the V transpose
-    static_assert(CK >= 1 && NKG * (D / 8) == NT, "staging covers the tile");
+    constexpr int IPW = KB / RPI / (2 * WQ);  // DMA instructions per wave, operand and block
+    static_assert(IPW >= 1 && IPW * RPI * 2 * WQ == KB, "the waves' DMAs cover a tile");
     constexpr int NR = NB * 16 + 2;        // floats per lane of a partial: O^T, m, l
-    // LDS: two block buffers; after the loop the same bytes hold the merge data.
+    // LDS: two block buffers and the merge area, separate objects so that the compiler
+    // can tell a DMA into one buffer from reads of the other (it would otherwise wait for
+    // every DMA in flight before each read). One workgroup per CU either way (registers).
     constexpr int MERGEB = WQ * 64 * NR * 4;
-    constexpr int LDSB = 2 * STG > MERGEB ? 2 * STG : MERGEB;
-    __shared__ __attribute__((aligned(16))) char lds[LDSB];
+    __shared__ __attribute__((aligned(1024))) char buf0[STG];
+    __shared__ __attribute__((aligned(1024))) char buf1[STG];
+    __shared__ __attribute__((aligned(16))) char mgs[MERGEB];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -213,69 +216,82 @@ __global__ __launch_bounds__(128 * WQ, 2) void attn_kernel(AttnParams p) {
     // This wave needs keys < wave_kend; a wave whose rows all lie past the last token needs none.
     const int wave_kend = wfirst >= p.M ? 0 : CAUSAL ? min(p.Nk, p.pos0 + wlast + 1) : p.Nk;
 
-    // Global -> registers through buffer loads whose bound is the end of the last key (or
-    // value) row, so keys past Nk read as zeros (they are masked below) and never touch
-    // memory past the operand; the per-thread offsets are fixed, plus the block's row offset.
-    // K: chunk i of thread t is key (t + NT i) / (D/8), d offset 8 * ((t + NT i) % (D/8))
-    // (rows read whole). V: thread t holds keys R*kg .. R*kg+R-1 (kg = t % NKG) at
-    // d 8*dv .. 8*dv+7 (dv = t / NKG), ready to be written transposed.
-    const int kg = tid % NKG, dv = tid / NKG;
-    const uint32_t k_bytes = (uint32_t)(((int64_t)(p.Nk - 1) * p.ldk + D) * 2);
-    const uint32_t v_bytes = (uint32_t)(((int64_t)(p.Nk - 1) * p.ldv + D) * 2);
-    uint32_t koff[CK], voff[R];
+    // Chunk c of row r of a K or V tile sits at chunk position c ^ swz(r): any 8 (with 16
+    // chunks a row, any 16) consecutive rows from a multiple of 8 give distinct positions
+    // (the K fragment reads: one chunk of 32 consecutive rows), and the 4 rows of a
+    // 4-key run give distinct chunk pairs (the transpose reads: 32 bytes of each of 4 rows).
+    auto swz = [](int r) { return ((r & 3) << 1) | ((r >> 2) & 1) | (CPR >= 16 ? (r & 8) : 0); };
+
+    // DMA: wave w fills rows w * IPW * RPI .. of both tiles, instruction j the RPI rows from
+    // row0(j) = (w * IPW + j) * RPI into 1 KB of LDS; lane i writes chunk position i % CPR
+    // of row row0(j) + i / CPR, so it fetches the chunk that belongs there. Rows past the
+    // last key repeat the last key's row (finite values; those keys are masked).
+    const int wrow0 = wave * IPW * RPI;
+    int drow[IPW], dcol[IPW];
 #pragma unroll
-    for (int i = 0; i < CK; ++i) {
-        const int ch = tid + NT * i;
-        koff[i] = (uint32_t)(((ch / (D / 8)) * p.ldk + 8 * (ch % (D / 8))) * 2);
+    for (int j = 0; j < IPW; ++j) {
+        drow[j] = wrow0 + j * RPI + lane / CPR;
+        dcol[j] = ((lane % CPR) ^ swz(drow[j])) * 8;
     }
+    auto dma = [&](int kb, char* buf) {
+#if defined(__HIP_DEVICE_COMPILE__)
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<bf16*>(K), (short)0, (int)(((int64_t)(p.Nk - 1) * p.ldk + D) * 2), 0x00020000);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<bf16*>(V), (short)0, (int)(((int64_t)(p.Nk - 1) * p.ldv + D) * 2), 0x00020000);
 #pragma unroll
-    for (int j = 0; j < R; ++j) voff[j] = (uint32_t)(((R * kg + j) * p.ldv + 8 * dv) * 2);
-    bf16x8 kr[CK], vr[R];
-    auto fetch = [&](int kb) {
-        const uint32_t ko = (uint32_t)(kb * KB * p.ldk * 2), vo = (uint32_t)(kb * KB * p.ldv * 2);
-#pragma unroll
-        for (int i = 0; i < CK; ++i) kr[i] = load16(K, k_bytes, koff[i] + ko);
-#pragma unroll
-        for (int j = 0; j < R; ++j) vr[j] = load16(V, v_bytes, voff[j] + vo);
+        for (int j = 0; j < IPW; ++j) {
+            const int t = min(kb * KB + drow[j], p.Nk - 1);
+            char* l = buf + (wrow0 + j * RPI) * ROWB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)l, 16,
+                                                     (uint32_t)((t * p.ldk + dcol[j]) * 2), 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(l + TILE), 16,
+                                                     (uint32_t)((t * p.ldv + dcol[j]) * 2), 0, 0, 0);
+        }
+#endif
     };
-    auto stage = [&](char* buf) {
-#pragma unroll
-        for (int i = 0; i < CK; ++i) {
-            const int ch = tid + NT * i;
-            *reinterpret_cast<bf16x8*>(buf + (ch / (D / 8)) * KP + (ch % (D / 8)) * 16) = kr[i];
-        }
-        char* vt = buf + KT + vpos(R * kg) * 2;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            if constexpr (R == 4) {
-                const bf16x4 w = {vr[0][e], vr[1][e], vr[2][e], vr[3][e]};
-                *reinterpret_cast<bf16x4*>(vt + (8 * dv + e) * VP) = w;
-            } else if constexpr (R == 2) {
-                typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-                const bf16x2 w = {vr[0][e], vr[1][e]};
-                *reinterpret_cast<bf16x2*>(vt + (8 * dv + e) * VP) = w;
-            } else {
-                *reinterpret_cast<bf16*>(vt + (8 * dv + e) * VP) = vr[0][e];
-            }
-        }
+    // Every wave's DMAs of the older block have landed and every wave's LDS reads are done.
+    // The waits are explicit (a full fence would also wait for the younger block's DMAs),
+    // and the signal fences keep the compiler from moving memory accesses across.
+    auto block_barrier = [&](bool one_block_ahead) {
+        if (one_block_ahead)
+            __builtin_amdgcn_s_waitcnt(kLgkm0Vm(2 * IPW));
+        else
+            __builtin_amdgcn_s_waitcnt(kLgkm0Vm(0));
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
     };
 
-    if (kb0 < nkb) {
-        fetch(kb0);
-        stage(lds + (kb0 & 1) * STG);
-        __syncthreads();
-        if (kb0 + 1 < nkb) fetch(kb0 + 1);
+    // Fragment offsets. K: row 32 kh + l32, chunk 2 j + lh. V (transpose read, O^T block b,
+    // step st): lane group g = lane / 16 covers head-dim columns 32 b + 16 (g % 2) .. +15
+    // and, as source, its lane s = lane % 16 points at key 32 kh + 16 st + 4 (g / 2) + s / 4
+    // (+ 8 for the second read), columns 32 b + 16 (g % 2) + 4 (s % 4) .. +3.
+    const int krow = (32 * kh + l32) * ROWB, ksw = swz(l32);
+    const int g16 = lane >> 4, s16 = lane & 15;
+    const int vr1 = 32 * kh + 4 * (g16 >> 1) + (s16 >> 2), vr2 = vr1 + 8;
+    int voff1[NB], voff2[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const int c = 4 * b + 2 * (g16 & 1) + ((s16 & 3) >> 1);
+        voff1[b] = vr1 * ROWB + ((c ^ swz(vr1)) << 4) + (s16 & 1) * 8;
+        voff2[b] = vr2 * ROWB + ((c ^ swz(vr2)) << 4) + (s16 & 1) * 8;
     }
-    for (int kb = kb0; kb < nkb; ++kb) {
-        const char* ks = lds + (kb & 1) * STG;
-        const char* vts = ks + KT;
+
+    // Block kb is in `cur`, block kb + 1 in the other buffer (in flight); after the barrier
+    // that ends block kb, block kb + 2 goes into `cur`. The barrier and its wait are
+    // unconditional and each loop trip runs both buffers' steps, so the compiler sees every
+    // DMA into a buffer retired before that buffer's next reads and adds no waits of its own.
+    auto step = [&](int kb, char* cur) {
+        const char* ks = cur;
+        const char* vs = cur + TILE;
         const int k0 = kb * KB + 32 * kh;  // this wave's 32 keys
         if (k0 < wave_kend) {  // uniform per wave: past this wave's last query otherwise
             // S^T = K Q^T; all K fragments are read first so the LDS latency overlaps.
             bf16x8 kf[NC];
 #pragma unroll
             for (int j = 0; j < NC; ++j)
-                kf[j] = *reinterpret_cast<const bf16x8*>(ks + (32 * kh + l32) * KP + (16 * j + 8 * lh) * 2);
+                kf[j] = *reinterpret_cast<const bf16x8*>(ks + krow + (((2 * j + lh) ^ ksw) << 4));
             floatx16 s;
 #pragma unroll
             for (int e = 0; e < 16; ++e) s[e] = 0.f;
@@ -288,8 +304,11 @@ __global__ __launch_bounds__(128 * WQ, 2) void attn_kernel(AttnParams p) {
 #pragma unroll
             for (int st = 0; st < 2; ++st)
 #pragma unroll
-                for (int b = 0; b < NB; ++b)
-                    vf[st][b] = *reinterpret_cast<const bf16x8*>(vts + (32 * b + l32) * VP + (32 * kh + 16 * st + 8 * lh) * 2);
+                for (int b = 0; b < NB; ++b) {
+                    const bf16x4 lo = ld_tr(vs + st * 16 * ROWB + voff1[b]);
+                    const bf16x4 hi = ld_tr(vs + st * 16 * ROWB + voff2[b]);
+                    vf[st][b] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                }
 
             // Masks (keys past Nk; causal: keys after the query's position), only where a key
             // can fail them.
@@ -335,20 +354,25 @@ __global__ __launch_bounds__(128 * WQ, 2) void attn_kernel(AttnParams p) {
                 for (int b = 0; b < NB; ++b)
                     acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[st][b], pf[st], acc[b], 0, 0, 0);
         }
-        if (kb + 1 < nkb) {
-            // The other buffer was last read in the previous block, which every wave
-            // finished before the previous barrier.
-            stage(lds + ((kb + 1) & 1) * STG);
-            __syncthreads();
-            if (kb + 2 < nkb) fetch(kb + 2);
-        }
+        block_barrier(false);  // block kb + 1 is in; `cur` is free
+        if (kb + 2 < nkb) dma(kb + 2, cur);
+    };
+    if (kb0 < nkb) {
+        dma(kb0, buf0);
+        if (kb0 + 1 < nkb) dma(kb0 + 1, buf1);
+        block_barrier(kb0 + 1 < nkb);
     }
+    int kb = kb0;
+    for (; kb + 1 < nkb; kb += 2) {
+        step(kb, buf0);
+        step(kb + 1, buf1);
+    }
+    if (kb < nkb) step(kb, buf0);
 
     // Merge the two key halves: wave w + WQ leaves (m, l, O^T) in LDS, wave w combines.
     // Lane order in the merge area: [wave slice][register][lane], conflict-free.
     l_run = halves_sum(l_run);
-    __syncthreads();  // every wave is done with the block buffers
-    float* mg = reinterpret_cast<float*>(lds) + wq * 64 * NR;
+    float* mg = reinterpret_cast<float*>(mgs) + wq * 64 * NR;
     if (kh == 1) {
 #pragma unroll
         for (int b = 0; b < NB; ++b)
