@@ -45,7 +45,6 @@
 // bf16 where it becomes the P*V product's MFMA operand (the normaliser l sums the fp32
 // weights), and A_r is rounded once to bf16.
 #include <algorithm>
-#include <vector>
 #include <type_traits>
 
 #include "tp_internal.h"
@@ -67,21 +66,25 @@ struct AttnParams {
     // A workgroup holds 128 query rows of one query block: PACK = false, 128 tokens of one
     // query head; PACK = true (few tokens, e.g. decode), rows = (token, head) pairs of one
     // KV group, row r = token r / Gq, head g * Gq + r % Gq (Gq = hq / hk), so the group's
-    // query heads share every K/V block. The keys of a query block (nkb blocks of 64)
-    // are cut in ceil(nkb / L) near-equal ranges, one workgroup each (L = 0: no cut);
-    // each leaves its unnormalised partial in ws, and the last of a query block to
-    // arrive merges them in range order and stores.
-    // With PACK the ranges leave their partials with plain stores and attn_merge_kernel, the
-    // next launch, merges them: O^T rows at ws[slot][row][d], (m, l) at ws[ml_off + (slot *
-    // 128 + row) * 2].
+    // query heads share every K/V block.
+    // PACK: the keys of a query block (nkb blocks of 64) are cut in ceil(nkb / L) near-equal
+    // ranges, one workgroup each (L = 0: no cut); each leaves its unnormalised partial with
+    // plain stores and attn_merge_kernel, the next launch, merges them: O^T rows at
+    // ws[slot][row][d], (m, l) at ws[ml_off + (slot * 128 + row) * 2].
+    // Without PACK, L > 0: the same cut, one workgroup per range; a query block's ranges
+    // leave their unnormalised partials in ws and the last of them to arrive merges them in
+    // key order. With an order table the workgroups take the ranges largest first (entry =
+    // 4 * block + range, heads the minor index of blockIdx), so the hardware's in-order
+    // dispatch approximates longest-processing-time scheduling.
+    // Without PACK, nwg > 0: the work is U key blocks in a fixed order (head-major; within a
+    // head the query blocks in pairs nqb - 1, 0, nqb - 2, 1, ..., each in key order), and
+    // workgroup i takes the contiguous run [i U / nwg, (i + 1) U / nwg): every workgroup the
+    // same work, one per CU. A query block split between workgroups is merged as above.
     int L;
+    int U, nwg;
     float* ws;          // partial slots: (slot of the range) * (heads or KV groups) + head or group
     unsigned* counters; // one arrival counter per (query block, head) (without PACK)
     int64_t ml_off;
-    // Without PACK and with cut blocks: the workgroups' (query block, range) pairs, largest
-    // range first (entry = 4 * block + range; heads are the minor index of blockIdx), so
-    // the hardware's in-order dispatch schedules the longest work first. nord = 0: the
-    // order of the scalar walk below.
     int nord;
     unsigned short ord[768];
 };
@@ -111,8 +114,9 @@ __device__ __forceinline__ bf16x4 ld_tr(const char* a) {
 #endif
 }
 
-// s_waitcnt immediate: vmcnt(n) (n < 16) and lgkmcnt(0).
+// s_waitcnt immediates: vmcnt(n) (n < 16) and lgkmcnt(0); lgkmcnt(0) alone.
 constexpr unsigned kLgkm0Vm(int n) { return (unsigned)(n | (0x7 << 4)); }
+constexpr unsigned kLgkm0 = 0xC07F;
 
 template <int D, bool CAUSAL, bool PACK, int WQ>
 __global__ __launch_bounds__(128 * WQ, 2) void attn_kernel(AttnParams p) {
@@ -136,6 +140,7 @@ __global__ __launch_bounds__(128 * WQ, 2) void attn_kernel(AttnParams p) {
     __shared__ __attribute__((aligned(1024))) char buf0[STG];
     __shared__ __attribute__((aligned(1024))) char buf1[STG];
     __shared__ __attribute__((aligned(16))) char mgs[MERGEB];
+    __shared__ unsigned is_last;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -149,34 +154,12 @@ __global__ __launch_bounds__(128 * WQ, 2) void attn_kernel(AttnParams p) {
     auto last_tok = [&](int b) { return PACK ? min(p.M - 1, ((b + 1) * QB - 1) / gq) : min(p.M - 1, (b + 1) * QB - 1); };
     auto kend_of = [&](int b) { return CAUSAL ? min(p.Nk, p.pos0 + last_tok(b) + 1) : p.Nk; };
 
-    // Workgroup -> (head or KV group, query block, key range): blockIdx = piece * HM + hm.
-    // With an order table the piece is ord[blockIdx / HM] (slots: four per query block);
-    // otherwise pieces are enumerated from the last (longest, when causal) query block down
-    // and, within one, in key order (base = the slot of this query block's first piece).
-    const int hm = blockIdx.x % HM;
-    int qblk, np = 1, part = 0, base = 0;
-    if (!PACK && p.nord > 0) {
-        const int e = p.ord[blockIdx.x / HM];
-        qblk = e >> 2;
-        part = e & 3;
-        np = (kend_of(qblk) - 1) / KB / p.L + 1;  // ceil(nkb / L)
-        base = 4 * qblk;                           // partial slots: four per query block
-    } else {
-        int b = blockIdx.x / HM;
-        if (p.L > 0) {
-            // A scalar walk over the query blocks; its length grows like L, i.e. like the
-            // work of every piece, so its share stays small.
-            for (qblk = nqb - 1;; --qblk) {
-                np = ((kend_of(qblk) - 1) / KB + p.L) / p.L;  // ceil(nkb / L)
-                if (b < np) break;
-                b -= np;
-                base += np;
-            }
-            part = b;
-        } else {
-            qblk = nqb - 1 - b;
-        }
-    }
+    auto nkb_of = [&](int b) { return (kend_of(b) + KB - 1) / KB; };
+
+    // One piece of work: key blocks [kb0, nkb) of query block qblk for head (or KV group)
+    // hm; part `part` of the np parts of that query block, whose partial slots start at base.
+    auto piece = [&](const int hm, const int qblk, const int np, const int part, const int base, const int kb0,
+                     const int nkb) {
     const int g = PACK ? hm : hm / gq;  // KV head
     const int row = qblk * QB + wq * 32 + l32;         // this lane's query row
     const int qi = PACK ? row / gq : row;              // its token
@@ -209,10 +192,6 @@ __global__ __launch_bounds__(128 * WQ, 2) void attn_kernel(AttnParams p) {
         for (int e = 0; e < 16; ++e) acc[b][e] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
-    // Key blocks: all keys, or (causal) those up to the block's last query.
-    const int nkb_all = (kend_of(qblk) + KB - 1) / KB;
-    const int kb0 = part * nkb_all / np;
-    const int nkb = (part + 1) * nkb_all / np;  // this workgroup's blocks: [kb0, nkb)
     // This wave needs keys < wave_kend; a wave whose rows all lie past the last token needs none.
     const int wave_kend = wfirst >= p.M ? 0 : CAUSAL ? min(p.Nk, p.pos0 + wlast + 1) : p.Nk;
 
@@ -250,14 +229,14 @@ __global__ __launch_bounds__(128 * WQ, 2) void attn_kernel(AttnParams p) {
         }
 #endif
     };
-    // Every wave's DMAs of the older block have landed and every wave's LDS reads are done.
-    // The waits are explicit (a full fence would also wait for the younger block's DMAs),
-    // and the signal fences keep the compiler from moving memory accesses across.
-    auto block_barrier = [&](bool one_block_ahead) {
-        if (one_block_ahead)
-            __builtin_amdgcn_s_waitcnt(kLgkm0Vm(2 * IPW));
-        else
+    // Every wave's DMAs issued so far have landed (vm) and its LDS reads are done; then the
+    // waves meet. The waits are explicit (a full fence would add its own), and the signal
+    // fences keep the compiler from moving memory accesses across.
+    auto block_barrier = [&](bool vm) {
+        if (vm)
             __builtin_amdgcn_s_waitcnt(kLgkm0Vm(0));
+        else
+            __builtin_amdgcn_s_waitcnt(kLgkm0);
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_s_barrier();
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -279,9 +258,12 @@ __global__ __launch_bounds__(128 * WQ, 2) void attn_kernel(AttnParams p) {
     }
 
     // Block kb is in `cur`, block kb + 1 in the other buffer (in flight); after the barrier
-    // that ends block kb, block kb + 2 goes into `cur`. The barrier and its wait are
-    // unconditional and each loop trip runs both buffers' steps, so the compiler sees every
-    // DMA into a buffer retired before that buffer's next reads and adds no waits of its own.
+    // that ends block kb, block kb + 2 goes into `cur`. Every wait for DMAs is unconditional
+    // (the first block's before the second is requested: with both in flight and a wait
+    // for the older, the compiler split the tests of kb0 + 1 < nkb into separate branches,
+    // saw a path with no wait and waited for every DMA before the loop's reads) and each
+    // loop trip runs both buffers' steps, so on every path the compiler sees a buffer's
+    // DMAs retired before that buffer's next reads and adds no waits of its own.
     auto step = [&](int kb, char* cur) {
         const char* ks = cur;
         const char* vs = cur + TILE;
@@ -354,13 +336,14 @@ __global__ __launch_bounds__(128 * WQ, 2) void attn_kernel(AttnParams p) {
                 for (int b = 0; b < NB; ++b)
                     acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[st][b], pf[st], acc[b], 0, 0, 0);
         }
-        block_barrier(false);  // block kb + 1 is in; `cur` is free
+        block_barrier(true);  // block kb + 1 is in; `cur` is free
         if (kb + 2 < nkb) dma(kb + 2, cur);
     };
     if (kb0 < nkb) {
         dma(kb0, buf0);
-        if (kb0 + 1 < nkb) dma(kb0 + 1, buf1);
-        block_barrier(kb0 + 1 < nkb);
+        __builtin_amdgcn_s_waitcnt(kLgkm0Vm(0));  // block kb0 is in
+        if (kb0 + 1 < nkb) dma(kb0 + 1, buf1);    // lands under block kb0's work
+        block_barrier(false);
     }
     int kb = kb0;
     for (; kb + 1 < nkb; kb += 2) {
@@ -425,7 +408,6 @@ __global__ __launch_bounds__(128 * WQ, 2) void attn_kernel(AttnParams p) {
         // device-scope atomic stores and loads, coherent across the XCDs' L2 caches by
         // themselves; waiting for the stores before the arrival counter is incremented
         // orders them.
-        __shared__ unsigned is_last;
         auto slot = [&](int part_) { return p.ws + ((int64_t)(base + part_) * HM + hm) * (WQ * 64 * NR) + wq * 64 * NR; };
         const int unit = (nqb - 1 - qblk) * HM + hm;
         if (kh == 0) {
@@ -478,6 +460,60 @@ __global__ __launch_bounds__(128 * WQ, 2) void attn_kernel(AttnParams p) {
                               (bf16)(acc[b][4 * q + 2] * inv), (bf16)(acc[b][4 * q + 3] * inv)};
             *reinterpret_cast<bf16x4*>(orow + 32 * b + 8 * q + 4 * lh) = v;
         }
+    };
+
+    if (!PACK && p.nwg > 0) {
+        // This workgroup's run of the work order, one piece per query block it touches.
+        const int i = blockIdx.x;
+        const int u0 = (int)((int64_t)i * p.U / p.nwg), u1 = (int)((int64_t)(i + 1) * p.U / p.nwg);
+        const int Uh = p.U / HM;
+        // The workgroup whose run holds unit x.
+        auto wg_of = [&](int x) { return (int)(((int64_t)(x + 1) * p.nwg + p.U - 1) / p.U) - 1; };
+        for (int u = u0; u < u1;) {
+            const int hm = u / Uh;
+            int r = u - hm * Uh, o = 0, qb, n;
+            for (;; ++o) {
+                qb = (o & 1) ? o / 2 : nqb - 1 - o / 2;
+                n = nkb_of(qb);
+                if (r < n) break;
+                r -= n;
+            }
+            const int first = wg_of(u - r);
+            const int np = wg_of(u - r + n - 1) - first + 1;
+            const int kb1 = min(n, r + (u1 - u));
+            if (u != u0) __syncthreads();  // the previous piece is done with LDS
+            piece(hm, qb, np, i - first, 4 * qb, r, kb1);
+            u += kb1 - r;
+        }
+    } else {
+        // Workgroup -> (head or KV group, query block, key range): blockIdx = range * HM + hm;
+        // the range is ord[blockIdx / HM], or, without a table, ranges are enumerated from
+        // the last query block down and, within one, in key order (base = the slot of this
+        // query block's first range).
+        const int hm = blockIdx.x % HM;
+        int b = blockIdx.x / HM, qblk, np = 1, base = 0;
+        if (!PACK && p.nord > 0) {
+            const int e = p.ord[b];
+            qblk = e >> 2;
+            b = e & 3;
+            np = (nkb_of(qblk) - 1 + p.L) / p.L;
+            base = 4 * qblk;  // partial slots: four per query block
+        } else if (p.L > 0) {
+            // A scalar walk over the query blocks; its length grows like L, i.e. like the
+            // work of every range, so its share stays small.
+            for (qblk = nqb - 1;; --qblk) {
+                np = (nkb_of(qblk) - 1 + p.L) / p.L;  // ceil(nkb / L)
+                if (b < np) break;
+                b -= np;
+                base += np;
+            }
+        } else {
+            qblk = nqb - 1 - b;
+            b = 0;
+        }
+        const int n = nkb_of(qblk);
+        piece(hm, qblk, np, b, base, b * n / np, (b + 1) * n / np);
+    }
 }
 
 constexpr int kWQ = 4;  // query slices per workgroup: 128 query rows, 8 waves
@@ -575,30 +611,102 @@ tp_status_t run_attn(AttnParams p, const Ctx& c) {
         const int last = PACK ? std::min(p.M - 1, ((b + 1) * QB - 1) / gq) : std::min(p.M - 1, (b + 1) * QB - 1);
         return CAUSAL ? std::min(p.Nk, p.pos0 + last + 1) : p.Nk;
     };
-    // Cutting keys: causal prefill, where a query block's work grows with its index, cuts
-    // every block into ranges of at most a third of the longest, which bounds every
-    // workgroup's share (the ranges then run largest first, see ord); few query blocks
-    // (decode) cut their keys so that the grid has about one workgroup per CU.
+    // Cutting keys. Decode (PACK): few query blocks, whose keys are cut so that the grid has
+    // about one workgroup per CU. Prefill (no PACK), causal (a query block's work grows with
+    // its index) or with too few query blocks to fill the chip: every query block is cut into
+    // ranges of at most L key blocks; if those ranges fit in one wave of resident workgroups
+    // they run as they are, otherwise the work order is cut into equal runs, one per resident
+    // workgroup slot (a second wave would leave the chip idle behind its longest ranges).
     const int nkb_max = (kend_of(nqb - 1) + KB - 1) / KB;
+    const int cus = device_cu_count();
+    // Resident workgroups per CU, from the kernel's registers and LDS against a CDNA4 CU:
+    // 512 VGPRs per SIMD lane (allocated in steps of 8), four SIMDs, 160 KB of LDS.
+    static const int occ = [] {
+        hipFuncAttributes a;
+        if (hipFuncGetAttributes(&a, reinterpret_cast<const void*>(attn_kernel<D, CAUSAL, PACK, kWQ>)) != hipSuccess ||
+            a.numRegs <= 0)
+            return 1;
+        const int vgprs = (a.numRegs + 7) / 8 * 8;
+        const int waves_per_simd = std::min(8, 512 / vgprs);
+        const int by_regs = 4 * waves_per_simd / (2 * kWQ);  // 2 kWQ waves per workgroup
+        const int by_lds = a.sharedSizeBytes > 0 ? (int)(160 * 1024 / a.sharedSizeBytes) : by_regs;
+        return std::max(1, std::min(by_regs, by_lds));
+    }();
+    const int64_t slots_max = (int64_t)cus * occ;  // resident workgroups
     p.L = 0;
+    p.U = 0;
+    p.nwg = 0;
+    p.nord = 0;
+    int64_t grid = (int64_t)nqb * HM;
+    int64_t slots = 0;  // partial slots per head or KV group
     if (PACK) {
         // About one workgroup per CU, at most 128 ranges per query block (the merge reads
         // up to 16 ranges per thread).
-        const int want = std::min(128, std::max(1, (device_cu_count() + nqb * HM - 1) / (nqb * HM)));
+        const int want = std::min(128, std::max(1, (cus + nqb * HM - 1) / (nqb * HM)));
         p.L = std::max(1, (nkb_max + want - 1) / want);
         if (p.L >= nkb_max) p.L = 0;
-    } else if (CAUSAL && nqb >= 4) {
-        p.L = (nkb_max + 2) / 3;  // at most 3 ranges (measured: 2 and 4 ranges are slower)
+        if (p.L > 0) {
+            int64_t ranges = 0;
+            for (int b = 0; b < nqb; ++b) ranges += ((kend_of(b) - 1) / KB + p.L) / p.L;
+            grid = ranges * HM;
+            slots = ranges;
+            p.ml_off = ranges * HM * QB * D;
+        }
+    } else {
+        int L = 0;
+        if (CAUSAL && nqb >= 4)
+            L = (nkb_max + 2) / 3;  // at most 3 ranges (measured: 2 and 4 ranges are slower)
+        else if (2 * grid <= slots_max && nkb_max >= 2) {
+            const int k = (int)std::min<int64_t>(4, slots_max / grid);  // ranges per query block
+            L = (nkb_max + k - 1) / k;
+        }
+        if (L > 0 && L < nkb_max) {
+            int64_t ranges = 0, U = 0;
+            for (int b = 0; b < nqb; ++b) {
+                const int n = (kend_of(b) + KB - 1) / KB;
+                ranges += (n - 1 + L) / L;
+                U += n;
+            }
+            U *= HM;
+            // Equal runs of at least a third of the longest query block, so a query block
+            // touches at most 4 runs (its partial slots). Only with one resident workgroup per
+            // CU: with two, ranges in largest-first order keep both busy better (measured, head
+            // size 64: 52.5 us against 56.0 us for equal runs at 4096 tokens, 16 heads).
+            const int64_t nwg = std::min<int64_t>(slots_max, U / ((nkb_max + 2) / 3));
+            if (occ == 1 && ranges * HM > slots_max && nwg > 1 && U < (int64_t(1) << 30)) {
+                p.U = (int)U;
+                p.nwg = (int)nwg;
+                grid = nwg;
+                slots = 4 * (int64_t)nqb;
+            } else {
+                p.L = L;
+                grid = ranges * HM;
+                slots = ranges;
+                if (ranges <= (int64_t)(sizeof(p.ord) / sizeof(p.ord[0]))) {
+                    // Largest ranges first (a cut block's ranges are shorter than an uncut
+                    // block of the same index, so the plain walk would queue long uncut blocks
+                    // behind short ranges); four slots per query block.
+                    struct Piece { int size, e; };
+                    Piece v[sizeof(p.ord) / sizeof(p.ord[0])];
+                    int nv = 0;
+                    for (int b = nqb - 1; b >= 0; --b) {
+                        const int n = (kend_of(b) + KB - 1) / KB;
+                        const int np = (n - 1 + L) / L;
+                        for (int q = 0; q < np; ++q) v[nv++] = {(q + 1) * n / np - q * n / np, 4 * b + q};
+                    }
+                    std::stable_sort(v, v + nv, [](const Piece& a, const Piece& b) { return a.size > b.size; });
+                    for (int i = 0; i < nv; ++i) p.ord[i] = (unsigned short)v[i].e;
+                    p.nord = nv;
+                    slots = 4 * (int64_t)nqb;
+                }
+            }
+        }
     }
     p.ws = nullptr;
     p.counters = nullptr;
-    int64_t pieces = nqb;
-    if (p.L > 0) {
-        pieces = 0;
-        for (int b = 0; b < nqb; ++b) pieces += ((kend_of(b) - 1) / KB + p.L) / p.L;
+    if (slots > 0) {
         // Partials: without PACK one slot of WQ x 64 lanes x (D/2 + 2) floats per workgroup;
         // with PACK 128 rows x (D + 2) floats.
-        const int64_t slots = PACK ? pieces : std::max<int64_t>(pieces, 4 * (int64_t)nqb);
         const size_t floats = (size_t)(slots * HM) * (PACK ? QB * (D + 2) : kWQ * 64 * (D / 2 + 2));
         const WsNeed need{floats, (size_t)nqb * HM};
         if (c.planning()) {
@@ -608,28 +716,10 @@ tp_status_t run_attn(AttnParams p, const Ctx& c) {
         if (!c.ws || !c.ws->covers(need)) return TP_ERR_WORKSPACE;
         p.ws = c.ws->partials;
         p.counters = c.ws->counters;
-        p.ml_off = (int64_t)pieces * HM * QB * D;
     } else if (c.planning()) {
         return TP_OK;
     }
-    // Causal prefill: largest ranges first (a cut block's halves are about half as long as
-    // an uncut block of the same index, so the plain walk would queue long uncut blocks
-    // behind short halves).
-    p.nord = 0;
-    if (!PACK && p.L > 0 && pieces <= (int64_t)(sizeof(p.ord) / sizeof(p.ord[0]))) {
-        struct Piece { int size, e; };
-        std::vector<Piece> v;
-        for (int b = nqb - 1; b >= 0; --b) {
-            const int nkb = (kend_of(b) - 1) / KB + 1;
-            const int np = (nkb - 1) / p.L + 1;
-            for (int q = 0; q < np; ++q) v.push_back({(q + 1) * nkb / np - q * nkb / np, 4 * b + q});
-        }
-        std::stable_sort(v.begin(), v.end(), [](const Piece& a, const Piece& b) { return a.size > b.size; });
-        for (size_t i = 0; i < v.size(); ++i) p.ord[i] = (unsigned short)v[i].e;
-        p.nord = (int)v.size();
-    }
-    hipLaunchKernelGGL((attn_kernel<D, CAUSAL, PACK, kWQ>), dim3((unsigned)(pieces * HM)), dim3(128 * kWQ), 0,
-                       c.stream, p);
+    hipLaunchKernelGGL((attn_kernel<D, CAUSAL, PACK, kWQ>), dim3((unsigned)grid), dim3(128 * kWQ), 0, c.stream, p);
     if (PACK && p.L > 0) {
         const tp_status_t st = hip_status();
         if (st != TP_OK) return st;

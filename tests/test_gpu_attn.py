@@ -1,8 +1,10 @@
 """GPU parity of the head-local attention core (causal, grouped-query) against the fp64
 oracle, through the C ABI: ragged token counts, both head sizes, the 70B shard's shape, and
 the real chain QKV projection -> attention core -> O partial. From 4 query blocks of 128 on
-(M >= 385) the causal core cuts its longer blocks in two key ranges merged through the work
-space (513, 700, 1000, 2048 tokens cover that path, the repeated 2048 call its counters)."""
+(M >= 385) the causal core cuts its longer blocks into key ranges merged through the work
+space (513, 700, 1000, 2048 tokens cover that path, the repeated 2048 call its counters), and
+non-causal calls with few query blocks cut theirs too; where the ranges would need more than
+one wave of resident workgroups, the work is cut into equal runs instead (2500 - 4096 tokens)."""
 import numpy as np
 import pytest
 import torch
@@ -53,6 +55,21 @@ def test_attention_core_70b_shard_shape_and_determinism():
     _, A2 = _core(qkv, M, hq, hk, d, True)
     assert torch.equal(A1, A2)
     assert err(A1, O.attention_core_shard(host64(qkv), hq, hk, d, True)) <= BF16_TOL
+
+
+@pytest.mark.parametrize("M,hq,hk,d", [(2900, 8, 1, 128), (3000, 6, 2, 128), (2500, 16, 4, 64)])
+def test_attention_core_equal_runs_schedule(M, hq, hk, d):
+    """Causal prefill whose key ranges would need more than one wave of resident workgroups:
+    the work order is cut into equal runs, so a workgroup takes pieces of two or more query
+    blocks and a query block is merged from up to 4 runs (odd and even query-block counts,
+    both head sizes). Every element against the oracle, a bitwise repeat (fixed merge order)."""
+    log_case("attention core equal runs", M, hq, hk, d)
+    qkv = I.activations(M, (hq + 2 * hk) * d, 630 + M)
+    buf, A1 = _core(qkv, M, hq, hk, d, True)
+    _, A2 = _core(qkv, M, hq, hk, d, True)
+    assert torch.equal(A1, A2)
+    assert err(A1, O.attention_core_shard(host64(qkv), hq, hk, d, True)) <= BF16_TOL
+    assert canaries_intact(buf, (M, hq * d))
 
 
 def test_attention_chain_qkv_core_o():
