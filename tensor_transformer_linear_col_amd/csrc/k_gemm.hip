@@ -591,8 +591,10 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void gemm_dtl_kernel(GemmPar
 
 // The S pieces of each split tile, summed in K order, then the tile's epilogue.
 // Workgroup (r, i) takes block row i of split tile r with the thread layout of the
-// GEMM kernel, so thread tid reads exactly the float4 groups it would have held.
-template <int TN, int TM, int WAVES_N, int WAVES_M, int ACT, bool BIAS, typename OutT>
+// GEMM kernel, so thread tid reads exactly the float4 groups it would have held. S is
+// a compile-time count so that every piece's loads of a block are in flight together
+// (one memory round trip per block, not one per piece).
+template <int TN, int TM, int WAVES_N, int WAVES_M, int ACT, bool BIAS, typename OutT, int S>
 __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void splitk_reduce_kernel(GemmParams p) {
     constexpr bool SWIGLU = ACT == kActSwiglu;
     constexpr int NWAVES = WAVES_N * WAVES_M, NT = NWAVES * 64;
@@ -611,25 +613,28 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void splitk_reduce_kernel(Ge
     const int64_t piece = (int64_t)R * NG * NT;  // float4s between pieces of one tile
 #pragma unroll
     for (int j = 0; j < BM; ++j) {
-        floatx4 g[4], u[4];
+        floatx4 g[S][4], u[S][4];
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-            g[qq] = src[((i * BM + j) * 4 + qq) * NT];
-            if (SWIGLU) u[qq] = src[(((i + (SWIGLU ? BN : 0)) * BM + j) * 4 + qq) * NT];
-        }
-        for (int sp = 1; sp < p.S; ++sp)
+        for (int sp = 0; sp < S; ++sp)
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq) {
-                g[qq] += src[sp * piece + ((i * BM + j) * 4 + qq) * NT];
-                if (SWIGLU) u[qq] += src[sp * piece + (((i + (SWIGLU ? BN : 0)) * BM + j) * 4 + qq) * NT];
+                g[sp][qq] = src[sp * piece + ((i * BM + j) * 4 + qq) * NT];
+                if (SWIGLU) u[sp][qq] = src[sp * piece + (((i + (SWIGLU ? BN : 0)) * BM + j) * 4 + qq) * NT];
+            }
+#pragma unroll
+        for (int sp = 1; sp < S; ++sp)
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                g[0][qq] += g[sp][qq];
+                if (SWIGLU) u[0][qq] += u[sp][qq];
             }
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
             float gv[4], uv[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                gv[e] = g[qq][e];
-                uv[e] = SWIGLU ? u[qq][e] : 0.f;
+                gv[e] = g[0][qq][e];
+                uv[e] = SWIGLU ? u[0][qq][e] : 0.f;
             }
             const int n_base = tn * TN + wn * WN + i * 32 + 8 * qq + 4 * lh;
             const int m = tm * TM + wm * WM + j * 32 + l32;
@@ -700,8 +705,16 @@ tp_status_t run_dtl(const LinearDesc& d, int cus, const Ctx& c) {
     const tp_status_t st = hip_status();
     if (st != TP_OK) return st;
     constexpr int BN = TN / WAVES_N / 32;
-    hipLaunchKernelGGL((splitk_reduce_kernel<TN, TM, WAVES_N, WAVES_M, ACT, BIAS, OutT>), dim3((unsigned)(R * BN)),
-                       dim3(NT), 0, c.stream, p);
+    const dim3 rgrid((unsigned)(R * BN));
+    if (S == 2)
+        hipLaunchKernelGGL((splitk_reduce_kernel<TN, TM, WAVES_N, WAVES_M, ACT, BIAS, OutT, 2>), rgrid, dim3(NT), 0,
+                           c.stream, p);
+    else if (S == 3)
+        hipLaunchKernelGGL((splitk_reduce_kernel<TN, TM, WAVES_N, WAVES_M, ACT, BIAS, OutT, 3>), rgrid, dim3(NT), 0,
+                           c.stream, p);
+    else
+        hipLaunchKernelGGL((splitk_reduce_kernel<TN, TM, WAVES_N, WAVES_M, ACT, BIAS, OutT, 4>), rgrid, dim3(NT), 0,
+                           c.stream, p);
     return hip_status();
 }
 
