@@ -195,11 +195,15 @@ __global__ __launch_bounds__(128 * WQ, 2) void attn_kernel(AttnParams p) {
     // This wave needs keys < wave_kend; a wave whose rows all lie past the last token needs none.
     const int wave_kend = wfirst >= p.M ? 0 : CAUSAL ? min(p.Nk, p.pos0 + wlast + 1) : p.Nk;
 
-    // Chunk c of row r of a K or V tile sits at chunk position c ^ swz(r): any 8 (with 16
-    // chunks a row, any 16) consecutive rows from a multiple of 8 give distinct positions
-    // (the K fragment reads: one chunk of 32 consecutive rows), and the 4 rows of a
-    // 4-key run give distinct chunk pairs (the transpose reads: 32 bytes of each of 4 rows).
-    auto swz = [](int r) { return ((r & 3) << 1) | ((r >> 2) & 1) | (CPR >= 16 ? (r & 8) : 0); };
+    // Chunk c of row r of a K or V tile sits at chunk position c ^ swz(r), chosen for 64
+    // banks of 4 bytes: the K fragment reads (one chunk of 16 consecutive rows per 256 bytes
+    // served) and the transpose reads (64 bytes of each of 4 consecutive rows per 32 lanes)
+    // then touch every bank once. 16 chunks a row (a row spans all banks): swz takes 16
+    // distinct values over 16 rows, and the 4 rows of a run fall in distinct 64-byte groups.
+    // 8 chunks a row (two rows share the banks): the same over rows of equal parity.
+    auto swz = [](int r) {
+        return CPR >= 16 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+    };
 
     // DMA: wave w fills rows w * IPW * RPI .. of both tiles, instruction j the RPI rows from
     // row0(j) = (w * IPW + j) * RPI into 1 KB of LDS; lane i writes chunk position i % CPR
