@@ -179,10 +179,6 @@ __global__ __launch_bounds__(128 * WQ, 2) void attn_kernel(AttnParams p) {
         const bf16* qrow = p.q + (int64_t)min(qi, p.M - 1) * p.ldq + (int64_t)h * D + 8 * lh;
 #pragma unroll
         for (int j = 0; j < NC; ++j) qf[j] = *reinterpret_cast<const bf16x8*>(qrow + 16 * j);
-        // Consume the loads here: otherwise the wait for them lands inside the key loop,
-        // where the in-order load counter would also wait for the next block's prefetch.
-#pragma unroll
-        for (int j = 0; j < NC; ++j) asm volatile("" ::"v"(qf[j]));
     }
 
     floatx16 acc[NB];
@@ -263,11 +259,11 @@ __global__ __launch_bounds__(128 * WQ, 2) void attn_kernel(AttnParams p) {
 
     // Block kb is in `cur`, block kb + 1 in the other buffer (in flight); after the barrier
     // that ends block kb, block kb + 2 goes into `cur`. Every wait for DMAs is unconditional
-    // (the first block's before the second is requested: with both in flight and a wait
-    // for the older, the compiler split the tests of kb0 + 1 < nkb into separate branches,
-    // saw a path with no wait and waited for every DMA before the loop's reads) and each
-    // loop trip runs both buffers' steps, so on every path the compiler sees a buffer's
-    // DMAs retired before that buffer's next reads and adds no waits of its own.
+    // and waits for all of them (with both first blocks in flight and a wait for the older
+    // one only, the compiler split the tests of kb0 + 1 < nkb into separate branches, saw a
+    // path with no wait and waited for every DMA before the loop's reads), and each loop
+    // trip runs both buffers' steps, so on every path the compiler sees a buffer's DMAs
+    // retired before that buffer's next reads and adds no waits of its own.
     auto step = [&](int kb, char* cur) {
         const char* ks = cur;
         const char* vs = cur + TILE;
@@ -344,10 +340,14 @@ __global__ __launch_bounds__(128 * WQ, 2) void attn_kernel(AttnParams p) {
         if (kb + 2 < nkb) dma(kb + 2, cur);
     };
     if (kb0 < nkb) {
+        // The queries and the first two blocks are in flight together; one unconditional
+        // wait covers all of them (so the wait for the queries does not land inside the key
+        // loop, where the in-order load counter would also wait for the next prefetch).
         dma(kb0, buf0);
-        __builtin_amdgcn_s_waitcnt(kLgkm0Vm(0));  // block kb0 is in
-        if (kb0 + 1 < nkb) dma(kb0 + 1, buf1);    // lands under block kb0's work
-        block_barrier(false);
+        if (kb0 + 1 < nkb) dma(kb0 + 1, buf1);
+#pragma unroll
+        for (int j = 0; j < NC; ++j) asm volatile("" ::"v"(qf[j]));
+        block_barrier(true);
     }
     int kb = kb0;
     for (; kb + 1 < nkb; kb += 2) {
