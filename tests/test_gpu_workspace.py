@@ -144,3 +144,39 @@ def test_layer_step_replays_under_graph_capture(kind):
         assert torch.equal(L.Y, eager_y), f"replay {rep}"
         assert torch.equal(L.Y1, eager_y1), f"replay {rep}"
     del g
+
+
+@pytest.mark.parametrize("M,hq,hk,d", [(4096, 8, 1, 128), (2500, 16, 4, 64)])
+def test_attention_core_replays_under_graph_capture(M, hq, hk, d):
+    """The causal attention core where its key pieces merge through the work space (4096
+    tokens, 8 heads: equal runs of the work order; 2500 tokens, head size 64: largest-first
+    ranges), captured once and replayed with eager calls in between: every replay equals the
+    eager result bitwise, so the arrival counters are back at zero after each run."""
+    log_case("graph capture attention core", M, hq, hk, d)
+    qkv = I.activations(M, (hq + 2 * hk) * d, 640 + M).cuda()
+    A = torch.empty(M, hq * d, dtype=torch.bfloat16, device="cuda")
+    with tp.tp_plan() as need:
+        tp.tp_attn_core_shard(qkv, A, M, hq, hk, d, 1, True)
+    assert need.partial_bytes > 0 and need.n_counters > 0
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        tp.tp_workspace_reserve(need.partial_bytes, need.n_counters)
+        tp.tp_attn_core_shard(qkv, A, M, hq, hk, d, 1, True)
+    torch.cuda.synchronize()
+    eager = A.clone()
+    assert err(eager.cpu(), O.attention_core_shard(host64(qkv.cpu()), hq, hk, d, True)) <= BF16_TOL
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        tp.tp_attn_core_shard(qkv, A, M, hq, hk, d, 1, True)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        A.fill_(float("nan"))
+        tp.tp_attn_core_shard(qkv, A, M, hq, hk, d, 1, True)  # eager, null stream
+        torch.cuda.synchronize()
+        assert torch.equal(A, eager)
+        A.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(A, eager), f"replay {rep}"
+    del g
