@@ -611,30 +611,34 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void splitk_reduce_kernel(Ge
     tile_coords(p.F + r, p.tiles_n, p.tiles_m, tn, tm);
     const floatx4* src = reinterpret_cast<const floatx4*>(p.ws) + (int64_t)r * NG * NT + tid;
     const int64_t piece = (int64_t)R * NG * NT;  // float4s between pieces of one tile
-#pragma unroll
-    for (int j = 0; j < BM; ++j) {
-        floatx4 g[S][4], u[S][4];
+    // Block (row block a, column block j): every piece's four float4 groups loaded, then
+    // summed in K order (the gate and up blocks of a SwiGLU tile one after the other, which
+    // keeps the registers within the 1024-thread budget).
+    auto sum_block = [&](int a, int j, floatx4 (&out)[4]) {
+        floatx4 x[S][4];
 #pragma unroll
         for (int sp = 0; sp < S; ++sp)
 #pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                g[sp][qq] = src[sp * piece + ((i * BM + j) * 4 + qq) * NT];
-                if (SWIGLU) u[sp][qq] = src[sp * piece + (((i + (SWIGLU ? BN : 0)) * BM + j) * 4 + qq) * NT];
-            }
+            for (int qq = 0; qq < 4; ++qq) x[sp][qq] = src[sp * piece + ((a * BM + j) * 4 + qq) * NT];
 #pragma unroll
-        for (int sp = 1; sp < S; ++sp)
+        for (int qq = 0; qq < 4; ++qq) {
+            out[qq] = x[0][qq];
 #pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                g[0][qq] += g[sp][qq];
-                if (SWIGLU) u[0][qq] += u[sp][qq];
-            }
+            for (int sp = 1; sp < S; ++sp) out[qq] += x[sp][qq];
+        }
+    };
+#pragma unroll
+    for (int j = 0; j < BM; ++j) {
+        floatx4 g[4], u[4];
+        sum_block(i, j, g);
+        if (SWIGLU) sum_block(i + (SWIGLU ? BN : 0), j, u);
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
             float gv[4], uv[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                gv[e] = g[0][qq][e];
-                uv[e] = SWIGLU ? u[0][qq][e] : 0.f;
+                gv[e] = g[qq][e];
+                uv[e] = SWIGLU ? u[qq][e] : 0.f;
             }
             const int n_base = tn * TN + wn * WN + i * 32 + 8 * qq + 4 * lh;
             const int m = tm * TM + wm * WM + j * 32 + l32;
@@ -679,7 +683,9 @@ tp_status_t run_dtl(const LinearDesc& d, int cus, const Ctx& c) {
     int S = 1;
     if (R > 0 && tiles * 10 < ceil_div(tiles, (int64_t)cus) * cus * 9) {
         double best = 2.0 / 3.0;
-        for (int s = 2; s <= 4 && kt / s >= 8; ++s) {
+        // Up to 8 ranges for plain products, 3 for the SwiGLU pair (twice the partials; its
+        // reduce holds 2 x S groups per thread within the 1024-thread register budget).
+        for (int s = 2; s <= (ACT == kActSwiglu ? 3 : 8) && kt / s >= 8; ++s) {
             const double tm = (double)ceil_div(R * s, (int64_t)cus) / s;
             if (tm < best - 1e-9) { best = tm; S = s; }
         }
@@ -712,9 +718,23 @@ tp_status_t run_dtl(const LinearDesc& d, int cus, const Ctx& c) {
     else if (S == 3)
         hipLaunchKernelGGL((splitk_reduce_kernel<TN, TM, WAVES_N, WAVES_M, ACT, BIAS, OutT, 3>), rgrid, dim3(NT), 0,
                            c.stream, p);
-    else
-        hipLaunchKernelGGL((splitk_reduce_kernel<TN, TM, WAVES_N, WAVES_M, ACT, BIAS, OutT, 4>), rgrid, dim3(NT), 0,
-                           c.stream, p);
+    else if constexpr (ACT != kActSwiglu) {
+        if (S == 4)
+            hipLaunchKernelGGL((splitk_reduce_kernel<TN, TM, WAVES_N, WAVES_M, ACT, BIAS, OutT, 4>), rgrid, dim3(NT), 0,
+                               c.stream, p);
+        else if (S == 5)
+            hipLaunchKernelGGL((splitk_reduce_kernel<TN, TM, WAVES_N, WAVES_M, ACT, BIAS, OutT, 5>), rgrid, dim3(NT), 0,
+                               c.stream, p);
+        else if (S == 6)
+            hipLaunchKernelGGL((splitk_reduce_kernel<TN, TM, WAVES_N, WAVES_M, ACT, BIAS, OutT, 6>), rgrid, dim3(NT), 0,
+                               c.stream, p);
+        else if (S == 7)
+            hipLaunchKernelGGL((splitk_reduce_kernel<TN, TM, WAVES_N, WAVES_M, ACT, BIAS, OutT, 7>), rgrid, dim3(NT), 0,
+                               c.stream, p);
+        else
+            hipLaunchKernelGGL((splitk_reduce_kernel<TN, TM, WAVES_N, WAVES_M, ACT, BIAS, OutT, 8>), rgrid, dim3(NT), 0,
+                               c.stream, p);
+    }
     return hip_status();
 }
 
@@ -792,8 +812,9 @@ tp_status_t launch_gemm(const LinearDesc& d, const Ctx& c) {
     // SIMD holds 2 (4) waves and one's MFMAs cover another's waits on the DMA and L2
     // misses (measured in the layer step, where each shard's weights come cold from
     // HBM: 907 -> 992 TFLOP/s over 4 waves of 128 x 128); the DMA kernel also takes
-    // fewer tiles than CUs once each CU gets at least 16 slices of split-K work.
-    // Otherwise register-staged 256 x 256 or 128 x 128 tiles.
+    // fewer tiles than CUs once each CU gets at least 16 (plain products: 8) slices of
+    // split-K work (70B QKV shard at 1024 tokens: 89 us on 80 register-staged 128 x 128
+    // tiles). Otherwise register-staged 256 x 256 or 128 x 128 tiles.
     const bool dma = d.K % DBK == 0;
     const int64_t kt = d.K / DBK;
     if (d.swiglu) {
@@ -806,7 +827,7 @@ tp_status_t launch_gemm(const LinearDesc& d, const Ctx& c) {
     const int64_t big = ceil_div(d.N, 256) * ceil_div(d.M, 256);
     auto plain = [&](auto act) -> tp_status_t {
         constexpr int A = decltype(act)::value;
-        if (dma && (big >= cus || big * kt >= 16 * (int64_t)cus))
+        if (dma && (big >= cus || big * kt >= 8 * (int64_t)cus))
             return run_dtl_bias<256, 256, 2, 4, A>(d, cus, c);
         if (big >= cus) return run_bias<256, 256, 2, 2, A>(d, c);
         return run_bias<128, 128, 2, 2, A>(d, c);

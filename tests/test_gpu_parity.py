@@ -419,10 +419,14 @@ def test_dma_kernel_swiglu_tails(M, K, I_):
     assert canaries_intact(buf, (M, I_))
 
 
-# ---- stream-K: fewer large tiles than CUs, so K is shared between workgroups ---------------
-# (the LDS-DMA kernel takes these once every CU gets at least 16 slices of 64).
+# ---- split K: fewer large tiles than CUs, so K is shared between workgroups ----------------
+# (the LDS-DMA kernel takes these once every CU gets at least 8 slices of 64, 16 for the SwiGLU
+# pair). K ranges per tile: (1000, 16384, 1320) 8 (24 tiles), (2048, 8192, 1280) 6 (40 tiles),
+# (4096, 8192, 1280) 3 (80 tiles), (1100, 3072, 2200) 5 (45 tiles), (1100, 4096, 1700) 7 (35
+# tiles), (1400, 4096, 2500) 4 (60 tiles), (1024, 8192, 1280) 8 (20 tiles); ragged M and N.
 
-@pytest.mark.parametrize("M,K,N", [(1000, 16384, 1320), (2048, 8192, 1280), (4096, 8192, 1280)])
+@pytest.mark.parametrize("M,K,N", [(1000, 16384, 1320), (2048, 8192, 1280), (4096, 8192, 1280), (1100, 3072, 2200),
+                                   (1100, 4096, 1700), (1400, 4096, 2500), (1024, 8192, 1280)])
 def test_stream_k_linear(M, K, N):
     log_case("stream-K linear", M, K, N)
     x, w, b = I.activations(M, K, 321), I.weight(N, K, 322), I.bias(N, 323)
