@@ -589,6 +589,18 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void gemm_dtl_kernel(GemmPar
                                                           acc[i][j][4 * qq + 2], acc[i][j][4 * qq + 3]};
 }
 
+// One float4 per lane from base + voff + soff (voff a lane register, soff uniform),
+// through a raw buffer descriptor of `bytes` bytes (device pass only, as dma_rows).
+__device__ __forceinline__ floatx4 load_f4(const void* base, uint32_t bytes, uint32_t voff, uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+    return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, soff, 0));
+#else
+    return floatx4{};
+#endif
+}
+
 // The S pieces of each split tile, summed in K order, then the tile's epilogue.
 // Workgroup (r, i) takes block row i of split tile r with the thread layout of the
 // GEMM kernel, so thread tid reads exactly the float4 groups it would have held. S is
@@ -609,8 +621,14 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void splitk_reduce_kernel(Ge
     const int r = blockIdx.x / BN, i = blockIdx.x - r * BN;
     int tn, tm;
     tile_coords(p.F + r, p.tiles_n, p.tiles_m, tn, tm);
-    const floatx4* src = reinterpret_cast<const floatx4*>(p.ws) + (int64_t)r * NG * NT + tid;
+    // The tile's partials, read through a buffer descriptor: one lane offset register
+    // for every load and the piece and group as a scalar offset (a 64-bit address per
+    // load in flight would take the registers the loads need). All offsets are below
+    // the descriptor's bound, the end of the tile's last piece.
+    const floatx4* src = reinterpret_cast<const floatx4*>(p.ws) + (int64_t)r * NG * NT;
     const int64_t piece = (int64_t)R * NG * NT;  // float4s between pieces of one tile
+    const uint32_t src_bytes = (uint32_t)(((S - 1) * piece + NG * NT) * (int64_t)sizeof(floatx4));
+    const uint32_t lane_off = (uint32_t)tid * sizeof(floatx4);
     // Block (row block a, column block j): every piece's four float4 groups loaded, then
     // summed in K order (the gate and up blocks of a SwiGLU tile one after the other, which
     // keeps the registers within the 1024-thread budget).
@@ -619,7 +637,9 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void splitk_reduce_kernel(Ge
 #pragma unroll
         for (int sp = 0; sp < S; ++sp)
 #pragma unroll
-            for (int qq = 0; qq < 4; ++qq) x[sp][qq] = src[sp * piece + ((a * BM + j) * 4 + qq) * NT];
+            for (int qq = 0; qq < 4; ++qq)
+                x[sp][qq] = load_f4(src, src_bytes, lane_off,
+                                    (uint32_t)((sp * piece + ((a * BM + j) * 4 + qq) * NT) * (int64_t)sizeof(floatx4)));
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
             out[qq] = x[0][qq];
@@ -631,6 +651,10 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void splitk_reduce_kernel(Ge
     for (int j = 0; j < BM; ++j) {
         floatx4 g[4], u[4];
         sum_block(i, j, g);
+        // The up blocks' loads stay behind the gate sums, and the next block's behind this
+        // block's stores (hoisted, they overflow the 128 registers a thread of a
+        // 1024-thread workgroup has).
+        if (SWIGLU) __builtin_amdgcn_sched_barrier(0);
         if (SWIGLU) sum_block(i + (SWIGLU ? BN : 0), j, u);
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
@@ -644,6 +668,7 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void splitk_reduce_kernel(Ge
             const int m = tm * TM + wm * WM + j * 32 + l32;
             epilogue4<ACT, BIAS, OutT>(p.o, n_base, m, gv, uv);
         }
+        if (SWIGLU) __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -683,9 +708,8 @@ tp_status_t run_dtl(const LinearDesc& d, int cus, const Ctx& c) {
     int S = 1;
     if (R > 0 && tiles * 10 < ceil_div(tiles, (int64_t)cus) * cus * 9) {
         double best = 2.0 / 3.0;
-        // Up to 8 ranges for plain products, 3 for the SwiGLU pair (twice the partials; its
-        // reduce holds 2 x S groups per thread within the 1024-thread register budget).
-        for (int s = 2; s <= (ACT == kActSwiglu ? 3 : 8) && kt / s >= 8; ++s) {
+        // Up to 8 ranges for plain products, 4 for the SwiGLU pair (twice the partials).
+        for (int s = 2; s <= (ACT == kActSwiglu ? 4 : 8) && kt / s >= 8; ++s) {
             const double tm = (double)ceil_div(R * s, (int64_t)cus) / s;
             if (tm < best - 1e-9) { best = tm; S = s; }
         }
@@ -718,11 +742,11 @@ tp_status_t run_dtl(const LinearDesc& d, int cus, const Ctx& c) {
     else if (S == 3)
         hipLaunchKernelGGL((splitk_reduce_kernel<TN, TM, WAVES_N, WAVES_M, ACT, BIAS, OutT, 3>), rgrid, dim3(NT), 0,
                            c.stream, p);
+    else if (S == 4)
+        hipLaunchKernelGGL((splitk_reduce_kernel<TN, TM, WAVES_N, WAVES_M, ACT, BIAS, OutT, 4>), rgrid, dim3(NT), 0,
+                           c.stream, p);
     else if constexpr (ACT != kActSwiglu) {
-        if (S == 4)
-            hipLaunchKernelGGL((splitk_reduce_kernel<TN, TM, WAVES_N, WAVES_M, ACT, BIAS, OutT, 4>), rgrid, dim3(NT), 0,
-                               c.stream, p);
-        else if (S == 5)
+        if (S == 5)
             hipLaunchKernelGGL((splitk_reduce_kernel<TN, TM, WAVES_N, WAVES_M, ACT, BIAS, OutT, 5>), rgrid, dim3(NT), 0,
                                c.stream, p);
         else if (S == 6)
@@ -812,9 +836,13 @@ tp_status_t launch_gemm(const LinearDesc& d, const Ctx& c) {
     // SIMD holds 2 (4) waves and one's MFMAs cover another's waits on the DMA and L2
     // misses (measured in the layer step, where each shard's weights come cold from
     // HBM: 907 -> 992 TFLOP/s over 4 waves of 128 x 128); the DMA kernel also takes
-    // fewer tiles than CUs once each CU gets at least 16 (plain products: 8) slices of
-    // split-K work (70B QKV shard at 1024 tokens: 89 us on 80 register-staged 128 x 128
-    // tiles). Otherwise register-staged 256 x 256 or 128 x 128 tiles.
+    // fewer tiles than CUs, split in K, once each CU gets at least 16 slices of work, or,
+    // for plain products with K >= 2048, 8 slices, or with K >= 4096 whenever 128 x 128
+    // tiles would leave half the CUs idle (70B QKV shard at 1024 / 512 tokens: 89 / 95 us
+    // on 80 / 40 register-staged 128 x 128 tiles). Short K stays off the split: its pieces
+    // cannot pay for the partials (O shard at 1024 tokens, K = 1024: 28 us as 512
+    // register-staged tiles, 47 us split). Otherwise register-staged 256 x 256 or
+    // 128 x 128 tiles.
     const bool dma = d.K % DBK == 0;
     const int64_t kt = d.K / DBK;
     if (d.swiglu) {
@@ -827,7 +855,9 @@ tp_status_t launch_gemm(const LinearDesc& d, const Ctx& c) {
     const int64_t big = ceil_div(d.N, 256) * ceil_div(d.M, 256);
     auto plain = [&](auto act) -> tp_status_t {
         constexpr int A = decltype(act)::value;
-        if (dma && (big >= cus || big * kt >= 8 * (int64_t)cus))
+        const int64_t small = ceil_div(d.N, 128) * ceil_div(d.M, 128);
+        if (dma && (big >= cus || big * kt >= 16 * (int64_t)cus || (kt >= 32 && big * kt >= 8 * (int64_t)cus) ||
+                    (kt >= 64 && 2 * small <= cus)))
             return run_dtl_bias<256, 256, 2, 4, A>(d, cus, c);
         if (big >= cus) return run_bias<256, 256, 2, 2, A>(d, c);
         return run_bias<128, 128, 2, 2, A>(d, c);
