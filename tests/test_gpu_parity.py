@@ -420,8 +420,8 @@ def test_dma_kernel_swiglu_tails(M, K, I_):
 
 
 # ---- split K: fewer large tiles than CUs, so K is shared between workgroups ----------------
-# (the LDS-DMA kernel takes these once every CU gets at least 8 slices of 64, 16 for the SwiGLU
-# pair). K ranges per tile: (1000, 16384, 1320) 8 (24 tiles), (2048, 8192, 1280) 6 (40 tiles),
+# (the LDS-DMA kernel takes these once every CU gets at least 16 slices of 64, or 8 for plain
+# products with K >= 2048). K ranges per tile: (1000, 16384, 1320) 8 (24 tiles), (2048, 8192, 1280) 6 (40 tiles),
 # (4096, 8192, 1280) 3 (80 tiles), (1100, 3072, 2200) 5 (45 tiles), (1100, 4096, 1700) 7 (35
 # tiles), (1400, 4096, 2500) 4 (60 tiles), (1024, 8192, 1280) 8 (20 tiles); ragged M and N.
 

@@ -28,9 +28,12 @@ def _cases():
             K = int(rng.integers(1, 1024)) * 8
             N = int(rng.integers(1, 5000))
             out.append((M, K, N, kind))
-    # large prefill shapes on the LDS-DMA kernel: whole waves of tiles, and split-K remainders
+    # large prefill shapes on the LDS-DMA kernel: whole waves of tiles, and split-K remainders;
+    # then long K on few tiles (8 K ranges of 10 or 8 tiles), the SwiGLU pair without biases in
+    # 4 ranges, and short K kept on register-staged tiles
     out += [(512, 4096, 16384, "col"), (1024, 8192, 1536, "col_bias"), (700, 6144, 2000, "swiglu_bias"),
-            (2048, 2048, 4100, "row_f32")]
+            (2048, 2048, 4100, "row_f32"), (512, 8192, 1280, "col"), (300, 4096, 1000, "row_f32"),
+            (512, 8192, 3584, "swiglu"), (1024, 1024, 8192, "col")]
     return out
 
 
