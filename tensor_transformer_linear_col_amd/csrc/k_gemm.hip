@@ -602,10 +602,10 @@ __device__ __forceinline__ floatx4 load_f4(const void* base, uint32_t bytes, uin
 }
 
 // The S pieces of each split tile, summed in K order, then the tile's epilogue.
-// Workgroup (r, i) takes block row i of split tile r with the thread layout of the
-// GEMM kernel, so thread tid reads exactly the float4 groups it would have held. S is
-// a compile-time count so that every piece's loads of a block are in flight together
-// (one memory round trip per block, not one per piece).
+// Workgroup (r, i, j) takes 32x32 block (i, j) of every wave's part of split tile r,
+// with the thread layout of the GEMM kernel, so thread tid reads exactly the float4
+// groups it would have held. S is a compile-time count so that every piece's loads are
+// in flight together: one memory round trip per workgroup.
 template <int TN, int TM, int WAVES_N, int WAVES_M, int ACT, bool BIAS, typename OutT, int S>
 __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void splitk_reduce_kernel(GemmParams p) {
     constexpr bool SWIGLU = ACT == kActSwiglu;
@@ -618,7 +618,8 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void splitk_reduce_kernel(Ge
     const int wn = wave % WAVES_N, wm = wave / WAVES_N;
     const int l32 = lane & 31, lh = lane >> 5;
     const int R = p.tiles_n * p.tiles_m - p.F;
-    const int r = blockIdx.x / BN, i = blockIdx.x - r * BN;
+    const int j = (int)blockIdx.x % BM, ri = (int)blockIdx.x / BM;
+    const int r = ri / BN, i = ri - r * BN;
     int tn, tm;
     tile_coords(p.F + r, p.tiles_n, p.tiles_m, tn, tm);
     // The tile's partials, read through a buffer descriptor: one lane offset register
@@ -630,9 +631,8 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void splitk_reduce_kernel(Ge
     const uint32_t src_bytes = (uint32_t)(((S - 1) * piece + NG * NT) * (int64_t)sizeof(floatx4));
     const uint32_t lane_off = (uint32_t)tid * sizeof(floatx4);
     // Block (row block a, column block j): every piece's four float4 groups loaded, then
-    // summed in K order (the gate and up blocks of a SwiGLU tile one after the other, which
-    // keeps the registers within the 1024-thread budget).
-    auto sum_block = [&](int a, int j, floatx4 (&out)[4]) {
+    // summed in K order (the gate and up blocks of a SwiGLU tile one after the other).
+    auto sum_block = [&](int a, floatx4 (&out)[4]) {
         floatx4 x[S][4];
 #pragma unroll
         for (int sp = 0; sp < S; ++sp)
@@ -647,15 +647,13 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void splitk_reduce_kernel(Ge
             for (int sp = 1; sp < S; ++sp) out[qq] += x[sp][qq];
         }
     };
-#pragma unroll
-    for (int j = 0; j < BM; ++j) {
+    {
         floatx4 g[4], u[4];
-        sum_block(i, j, g);
-        // The up blocks' loads stay behind the gate sums, and the next block's behind this
-        // block's stores (hoisted, they overflow the 128 registers a thread of a
-        // 1024-thread workgroup has).
+        sum_block(i, g);
+        // The up block's loads stay behind the gate sums (hoisted, they overflow the 128
+        // registers a thread of a 1024-thread workgroup has).
         if (SWIGLU) __builtin_amdgcn_sched_barrier(0);
-        if (SWIGLU) sum_block(i + (SWIGLU ? BN : 0), j, u);
+        if (SWIGLU) sum_block(i + (SWIGLU ? BN : 0), u);
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
             float gv[4], uv[4];
@@ -668,7 +666,6 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void splitk_reduce_kernel(Ge
             const int m = tm * TM + wm * WM + j * 32 + l32;
             epilogue4<ACT, BIAS, OutT>(p.o, n_base, m, gv, uv);
         }
-        if (SWIGLU) __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -734,8 +731,8 @@ tp_status_t run_dtl(const LinearDesc& d, int cus, const Ctx& c) {
                        dim3((unsigned)(F + R * S)), dim3(NT), 0, c.stream, p);
     const tp_status_t st = hip_status();
     if (st != TP_OK) return st;
-    constexpr int BN = TN / WAVES_N / 32;
-    const dim3 rgrid((unsigned)(R * BN));
+    constexpr int BN = TN / WAVES_N / 32, BM = TM / WAVES_M / 32;
+    const dim3 rgrid((unsigned)(R * BN * BM));
     if (S == 2)
         hipLaunchKernelGGL((splitk_reduce_kernel<TN, TM, WAVES_N, WAVES_M, ACT, BIAS, OutT, 2>), rgrid, dim3(NT), 0,
                            c.stream, p);
