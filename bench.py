@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--traffic-dma-check", action="store_true",
                     help="then one LDS-DMA GEMM whose every weight byte is read once (256 tokens x 65536 x 1024: "
                          "128 MiB of weights read, 32 MiB written), to check the calibration on DMA loads")
-    ap.add_argument("--decode-iters", type=int, default=100, help="launches per decode measurement")
+    ap.add_argument("--decode-iters", type=int, default=110, help="launches per decode measurement")
     return ap.parse_args()
 
 
