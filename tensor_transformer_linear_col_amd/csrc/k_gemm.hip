@@ -244,8 +244,8 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_kernel(GemmParams p) {
 // gfx950's buffer_load_dwordx4 ... lds writes each lane's 16 bytes straight into
 // LDS (at a wave-uniform LDS address + 16 * lane), so staging needs no registers and
 // the LDS ring can hold several BK-wide K slices while the matrix cores consume
-// one. Holding more than one slice in registers would not fit next to the
-// 128 x 128 accumulator tile of each wave.
+// one. Holding more than one slice in registers would not fit next to each wave's
+// accumulator tile.
 //
 // LDS row = BK bf16 = CPR chunks of 16 bytes. gfx950 serves a 16-byte-per-lane
 // LDS access 16 lanes (256 bytes, 64 banks) at a time; chunk c of row r is stored
@@ -696,7 +696,7 @@ tp_status_t run_dtl(const LinearDesc& d, int cus, const Ctx& c) {
     constexpr unsigned NT = WAVES_N * WAVES_M * 64;
     // One tile per workgroup when whole waves of tiles fill the chip to 90 %. Else
     // the whole waves stay one tile per workgroup and the R remaining tiles are cut
-    // into S K ranges, S (at most 4, at least 8 slices each) chosen so the pieces
+    // into S K ranges, S (at least 8 slices each) chosen so the pieces
     // take the least time on `cus` CUs: ceil(R*S / cus) / S tile times. A split is
     // only taken where it saves at least a third of a tile time: the partials cost
     // a pass of their own.
