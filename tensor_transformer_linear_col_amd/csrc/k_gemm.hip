@@ -669,6 +669,224 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void splitk_reduce_kernel(Ge
     }
 }
 
+// ---------------------------------------------------------------------------------
+// Plain products on 16-row MFMA blocks: v_mfma_f32_16x16x32_bf16, TN x TM tiles of 4
+// waves with (TN/2) x (TM/2) outputs each.
+//
+// 32-row blocks leave no good layout for a product whose 256 x 256 tiles do not fill
+// whole waves of CUs: the 70B TP=8 QKV shard (1280 features x 4096 tokens) has 80 such
+// tiles, which run as split-K pieces plus a reduce pass. With 16-row blocks the tile
+// can be 160 features x 128 tokens: 256 tiles, one per CU, each over the whole K, with
+// 80 x 64 outputs per wave (5 x 4 blocks: 9 fragment reads per 20 MFMAs).
+//
+// Operand staging as in gemm_dtl_kernel: K slices of 64 by LDS DMA into a ring of
+// STAGES buffers, each operand's rows dealt to whole waves; a wave whose operand runs
+// out of rows issues its remaining DMAs past the operand's bounds, where the buffer
+// descriptor's range check drops them, so every wave waits on the same counts.
+//
+// MFMA 16x16x32 operand mapping (lane l, l16 = l % 16, lq = l / 16):
+//   A: lane l holds W[n0 + l16][k0 + 8*lq .. +7];  B: lane l holds X[m0 + l16][k0 + 8*lq .. +7]
+//   D: register e of lane l holds D[n0 + 4*lq + e][m0 + l16]
+// ---------------------------------------------------------------------------------
+template <int TN, int TM>
+struct Dtl16Shape {
+    static constexpr int NWAVES = 4, NT = 256;
+    static constexpr int WN = TN / 2, WM = TM / 2;   // outputs per wave (2 x 2 waves)
+    static constexpr int NA = WN / 16, BM = WM / 16;  // 16-row blocks per wave
+    static constexpr int ROWB = DBK * 2, CPR = DBK / 8, RPW = 256 / ROWB, RPI = 64 / CPR;
+    static constexpr int waves_for(int ipw) { return (TN + ipw * RPI - 1) / (ipw * RPI) + (TM + ipw * RPI - 1) / (ipw * RPI); }
+    static constexpr int ipw_min() {
+        int i = ((TN + TM) / RPI + NWAVES - 1) / NWAVES;
+        while (waves_for(i) > NWAVES) ++i;
+        return i;
+    }
+    static constexpr int IPW = ipw_min();                  // DMA instructions per wave and slice
+    static constexpr int RPWV = IPW * RPI;                 // LDS rows per wave
+    static constexpr int W0 = (TN + RPWV - 1) / RPWV;      // waves loading weight rows
+    static constexpr int XB = W0 * RPWV;                   // first LDS row of the tokens
+    static constexpr int ROWS = NWAVES * RPWV;             // LDS rows per stage
+    static_assert(waves_for(IPW) == NWAVES, "the operands fill the waves");
+    static_assert(WN % 16 == 0 && WM % 16 == 0 && TN % RPI == 0 && TM % RPI == 0, "whole blocks and DMA rows");
+};
+
+template <int TN, int TM, int STAGES, bool BIAS, typename OutT>
+__global__ __launch_bounds__(256) void gemm_dtl16_kernel(GemmParams p) {
+    using Sh = Dtl16Shape<TN, TM>;
+    constexpr int NA = Sh::NA, BM = Sh::BM, WN = Sh::WN, WM = Sh::WM;
+    constexpr int ROWB = Sh::ROWB, CPR = Sh::CPR, RPW = Sh::RPW, RPI = Sh::RPI, IPW = Sh::IPW, RPWV = Sh::RPWV;
+    constexpr int STAGEB = Sh::ROWS * ROWB;
+    constexpr int KS = DBK / 32;  // MFMA sub-steps per slice
+    static_assert(KS == 2, "two sub-steps per slice alternate the fragment sets");
+    __shared__ __attribute__((aligned(1024))) char lds_raw[STAGES * STAGEB];
+    auto lds = reinterpret_cast<char (*)[STAGEB]>(lds_raw);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wn = wave & 1, wm = wave >> 1;
+    const int l16 = lane & 15, lq = lane >> 4;
+
+    int tn, tm;
+    tile_of(blockIdx.x, p.tiles_n, p.tiles_m, tn, tm);
+    const int n0 = tn * TN, m0 = tm * TM;
+
+    // This wave's DMA rows: operand rows t0 + j*RPI + lane/CPR into LDS rows
+    // wave*RPWV + j*RPI + lane/CPR; chunk c of LDS row r sits at c ^ ((r / RPW) % CPR).
+    const bool wop = wave < Sh::W0;
+    const int t0 = (wop ? wave : wave - Sh::W0) * RPWV;
+    const int orows = wop ? TN : TM;
+    const void* obase = wop ? (const void*)p.W0 : (const void*)p.X;
+    const int64_t obytes = wop ? (int64_t)p.N * p.K * 2 : (int64_t)(p.M - 1) * p.ldx * 2 + (int64_t)p.K * 2;
+    uint32_t goff[IPW];
+#pragma unroll
+    for (int j = 0; j < IPW; ++j) {
+        const int lr = j * RPI + lane / CPR;
+        const int row = wave * RPWV + lr;
+        const int c = (lane % CPR) ^ ((row / RPW) % CPR);
+        const int t = t0 + lr;
+        if (t0 + j * RPI >= orows) {
+            goff[j] = (uint32_t)obytes;  // past the operand: dropped by the range check
+        } else if (wop) {
+            goff[j] = (uint32_t)(((int64_t)min(n0 + t, p.N - 1) * p.K + c * 8) * 2);
+        } else {
+            goff[j] = (uint32_t)(((int64_t)min(m0 + t, p.M - 1) * p.ldx + c * 8) * 2);
+        }
+    }
+    const int KT = p.K / DBK;
+
+    // Fragment reads: block i of this lane is LDS row wn*WN + 16 i + l16 (weights) or
+    // XB + wm*WM + 16 j + l16 (tokens); every block starts on a multiple of 16 rows, so the
+    // swizzle term is (l16 / RPW) % CPR for all of them. Sub-step ks takes chunk 4 ks + lq.
+    const int sw = (l16 / RPW) % CPR;
+    const int abase = (wn * WN + l16) * ROWB;
+    const int bbase = (Sh::XB + wm * WM + l16) * ROWB;
+    floatx4 acc[NA][BM];
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+#pragma unroll
+        for (int j = 0; j < BM; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    auto read_frags = [&](const char* s, int ks, bf16x8 (&af)[NA], bf16x8 (&bfr)[BM]) {
+        const int kx = ((4 * ks + lq) ^ sw) * 16;
+#pragma unroll
+        for (int i = 0; i < NA; ++i) af[i] = *reinterpret_cast<const bf16x8*>(s + abase + i * 16 * ROWB + kx);
+#pragma unroll
+        for (int j = 0; j < BM; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(s + bbase + j * 16 * ROWB + kx);
+    };
+    auto mfmas = [&](bf16x8 (&af)[NA], bf16x8 (&bfr)[BM]) {
+#pragma unroll
+        for (int i = 0; i < NA; ++i)
+#pragma unroll
+            for (int j = 0; j < BM; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    };
+    auto sync_slice = [&](int ahead) {
+        static_assert(STAGES <= 4, "waits below cover up to 3 slices ahead");
+        if (ahead >= 3) __builtin_amdgcn_s_waitcnt(vmcnt_wait(3 * IPW));
+        else if (ahead == 2) __builtin_amdgcn_s_waitcnt(vmcnt_wait(2 * IPW));
+        else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vmcnt_wait(IPW));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    };
+    constexpr int NMF = NA * BM, NRD = NA + BM;
+    static_assert(NRD + IPW <= NMF, "every read and DMA of sub-step 0 follows an MFMA");
+    bf16x8 fa0[NA], fb0[BM], fa1[NA], fb1[BM];
+
+    // Prologue: every buffer requested; sub-step 0 of the first slice read.
+    for (int st = 0; st < STAGES && st < KT; ++st)
+        dma_rows<IPW>(obase, (uint32_t)obytes, goff, (uint32_t)(st * DBK * 2), &lds[st][wave * RPWV * ROWB]);
+    sync_slice(min(KT - 1, STAGES - 1));
+    read_frags(lds[0], 0, fa0, fb0);
+    __builtin_amdgcn_s_waitcnt(kLgkm0);
+    // Slice kt: sub-step 0 reads sub-step 1's fragments and refills the buffer slice kt-1
+    // left free (with slice kt-1+STAGES) behind its MFMAs; sub-step 1 synchronises on
+    // slice kt+1 and reads its sub-step 0.
+    auto slice = [&](int kt, auto refill_tag) {
+        constexpr bool REFILL = decltype(refill_tag)::value;
+        const char* s = lds[kt % STAGES];
+        read_frags(s, 1, fa1, fb1);
+        if (REFILL)
+            dma_rows<IPW>(obase, (uint32_t)obytes, goff, (uint32_t)((kt - 1 + STAGES) * DBK * 2),
+                          &lds[(kt + STAGES - 1) % STAGES][wave * RPWV * ROWB]);
+        mfmas(fa0, fb0);
+#pragma unroll
+        for (int q = 0; q < NMF; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            if (q < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+            else if (REFILL && q - NRD < IPW) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one DMA
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(kLgkm0);
+        // On the last slice this synchronises once more and reads a buffer nobody uses any
+        // more, so every slice takes the same path.
+        sync_slice(min(KT - 2 - kt, STAGES - 2));
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(lds[(kt + 1) % STAGES], 0, fa0, fb0);
+        mfmas(fa1, fb1);
+#pragma unroll
+        for (int q = 0; q < NMF; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (q < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(kLgkm0);
+    };
+    int kt = 0;
+    for (; kt == 0 && kt < KT; ++kt) slice(kt, std::false_type{});  // the prologue filled every buffer
+    for (; kt + STAGES - 1 < KT; ++kt) slice(kt, std::true_type{});
+    for (; kt < KT; ++kt) slice(kt, std::false_type{});
+
+    // Epilogue: register e of block (i, j) holds feature wn*WN + 16 i + 4 lq + e of token
+    // wm*WM + 16 j + l16; bias, one rounding, 4 consecutive outputs per store.
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+#pragma unroll
+        for (int j = 0; j < BM; ++j) {
+            float gv[4], uv[4] = {};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) gv[e] = acc[i][j][e];
+            const int n_base = n0 + wn * WN + 16 * i + 4 * lq;
+            const int m = m0 + wm * WM + 16 * j + l16;
+            epilogue4<kActNone, BIAS, OutT>(p.o, n_base, m, gv, uv);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+}
+
+template <int TN, int TM, bool BIAS, typename OutT>
+tp_status_t run_dtl16(const LinearDesc& d, const Ctx& c) {
+    if (c.planning()) return TP_OK;  // no work space
+    GemmParams p{};
+    p.X = static_cast<const bf16*>(d.X);
+    p.ldx = d.ldx;
+    p.W0 = static_cast<const bf16*>(d.W0);
+    p.W1 = nullptr;
+    p.o.Y = d.Y;
+    p.o.ldy = d.ldy;
+    p.o.M = (int)d.M;
+    p.o.N = (int)d.N;
+    p.o.b0 = static_cast<const bf16*>(d.b0);
+    p.o.b1 = nullptr;
+    p.o.vec_store = vec_store_ok<OutT>(d.Y, d.ldy);
+    p.o.vec16 = vec16_ok<OutT>(d.Y, d.ldy);
+    p.M = (int)d.M;
+    p.N = (int)d.N;
+    p.K = (int)d.K;
+    p.tiles_n = (int)ceil_div(d.N, TN);
+    p.tiles_m = (int)ceil_div(d.M, TM);
+    const int64_t tiles = (int64_t)p.tiles_n * p.tiles_m;
+    hipLaunchKernelGGL((gemm_dtl16_kernel<TN, TM, 3, BIAS, OutT>), dim3((unsigned)tiles), dim3(256), 0, c.stream, p);
+    return hip_status();
+}
+
+template <int TN, int TM>
+tp_status_t run_dtl16_bias(const LinearDesc& d, const Ctx& c) {
+    const bool bias = d.b0 != nullptr;
+    if (d.out_dtype == TP_DTYPE_BF16)
+        return bias ? run_dtl16<TN, TM, true, bf16>(d, c) : run_dtl16<TN, TM, false, bf16>(d, c);
+    return bias ? run_dtl16<TN, TM, true, float>(d, c) : run_dtl16<TN, TM, false, float>(d, c);
+}
+
 template <int TN, int TM, int WAVES_N, int WAVES_M, int ACT, bool BIAS, typename OutT>
 tp_status_t run_dtl(const LinearDesc& d, int cus, const Ctx& c) {
     GemmParams p;
@@ -853,6 +1071,13 @@ tp_status_t launch_gemm(const LinearDesc& d, const Ctx& c) {
     auto plain = [&](auto act) -> tp_status_t {
         constexpr int A = decltype(act)::value;
         const int64_t small = ceil_div(d.N, 128) * ceil_div(d.M, 128);
+        // Fewer 256 x 256 tiles than CUs, but whole waves of 160 x 128 tiles (filled to 90 %)
+        // and a long K: one tile per workgroup on 16-row MFMA blocks instead of K ranges and
+        // a reduce pass (the 70B TP=8 QKV shard at 4096 tokens: 256 tiles).
+        const int64_t t16 = ceil_div(d.N, 160) * ceil_div(d.M, 128);
+        if (dma && A == kActNone && big < cus && kt >= 32 && t16 >= cus &&
+            t16 * 10 >= ceil_div(t16, (int64_t)cus) * cus * 9)
+            return run_dtl16_bias<160, 128>(d, c);
         if (dma && (big >= cus || big * kt >= 16 * (int64_t)cus || (kt >= 32 && big * kt >= 8 * (int64_t)cus) ||
                     (kt >= 64 && 2 * small <= cus)))
             return run_dtl_bias<256, 256, 2, 4, A>(d, cus, c);

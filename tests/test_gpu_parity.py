@@ -419,6 +419,26 @@ def test_dma_kernel_swiglu_tails(M, K, I_):
     assert canaries_intact(buf, (M, I_))
 
 
+# 160 x 128 tiles on 16-row MFMA blocks: plain products with fewer 256 x 256 tiles than CUs
+# whose 160 x 128 tiles fill whole waves (the 70B TP=8 QKV shard's 1280 x 4096 outputs are 256
+# tiles); ragged features and tokens, bias or none, bf16 output or an fp32 row partial.
+@pytest.mark.parametrize("M,K,N,bias,f32", [(4096, 8192, 1280, True, False), (4000, 4096, 1250, True, False),
+                                            (3900, 2048, 2552, False, False), (4096, 2048, 1280, False, True)])
+def test_dtl16_tiles(M, K, N, bias, f32):
+    log_case("160x128 tiles on 16-row MFMA blocks", M, K, N, bias, f32)
+    x, w = I.activations(M, K, 361), I.weight(N, K, 362)
+    b = I.bias(N, 363) if bias else None
+    buf, Y = canary_buffer((M, N), torch.float32 if f32 else torch.bfloat16)
+    if f32:
+        tp.tp_linear_row_partial(dev(x), K, dev(w), Y, M, K, N, 1)
+    else:
+        tp.tp_linear_col(dev(x), dev(w), dev(b), Y, M, K, N, 1)
+    torch.cuda.synchronize()
+    ref = O.linear(host64(x), host64(w), None if b is None else host64(b))
+    assert err(Y.cpu(), ref) <= BF16_TOL
+    assert canaries_intact(buf, (M, N))
+
+
 # ---- split K: fewer large tiles than CUs, so K is shared between workgroups ----------------
 # (the LDS-DMA kernel takes these once every CU gets at least 16 slices of 64, or 8 for plain
 # products with K >= 2048). K ranges per tile: (1000, 16384, 1320) 8 (24 tiles), (2048, 8192, 1280) 6 (40 tiles),
