@@ -236,10 +236,13 @@ def test_dry_run_sizes_the_split_reductions(L):
     """A dry run validates, enqueues nothing (no GPU here, so any launch would fail with
     TP_ERR_HIP) and reports the largest work space of the calls inside it. Without a device
     the library plans for 256 compute units, as on MI355X."""
-    # 70B QKV shard at TP = 8 and 4096 tokens: 5 x 16 = 80 tiles of 256 x 256 on 256 CUs, each
-    # cut into 3 K ranges -> 240 fp32 partial tiles of 256 KB.
-    qkv = lambda: L.tp_attn_proj_shard(P, P, 0, P, 0, 0, 0, 4096, 8192, 64, 8, 128, 8, BF16, BF16, None)
+    # 70B QKV shard at TP = 8 and 2048 tokens: 5 x 8 = 40 tiles of 256 x 256 on 256 CUs, each
+    # cut into 6 K ranges -> 240 fp32 partial tiles of 256 KB.
+    qkv = lambda: L.tp_attn_proj_shard(P, P, 0, P, 0, 0, 0, 2048, 8192, 64, 8, 128, 8, BF16, BF16, None)
     assert _plan(L, qkv) == (OK, 240 * 256 * 256 * 4, 0)
+    # At 4096 tokens its 8 x 32 = 256 tiles of 160 x 128 fill the chip: no split, no work space.
+    qkv4k = lambda: L.tp_attn_proj_shard(P, P, 0, P, 0, 0, 0, 4096, 8192, 64, 8, 128, 8, BF16, BF16, None)
+    assert _plan(L, qkv4k) == (OK, 0, 0)
     # The same QKV shard at 8 tokens: 40 row groups of 32 outputs, K cut in 7 -> 280
     # workgroups with two 2 KB partial tiles each, and one arrival counter per row group.
     qkv1 = lambda: L.tp_attn_proj_shard(P, P, 0, P, 0, 0, 0, 8, 8192, 64, 8, 128, 8, BF16, BF16, None)
