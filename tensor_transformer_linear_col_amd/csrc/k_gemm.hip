@@ -24,6 +24,7 @@
 // MFMA 32x32x16 operand mapping (lane l, l32 = l % 32, lh = l / 32):
 //   A: lane l holds W[n0 + l32][k0 + 8*lh .. +7];  B: lane l holds X[m0 + l32][k0 + 8*lh .. +7]
 //   D: register e of lane l holds D[n0 + 8*(e/4) + 4*lh + e%4][m0 + l32]
+#include <algorithm>
 #include <type_traits>
 
 #include "tp_epilogue.h"
@@ -679,40 +680,67 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void splitk_reduce_kernel(Ge
 // can be 160 features x 128 tokens: 256 tiles, one per CU, each over the whole K, with
 // 80 x 64 outputs per wave (5 x 4 blocks: 9 fragment reads per 20 MFMAs).
 //
+// The same kernel takes 33-64 tokens as one 64-token tile (SK): 128-feature tiles, each
+// cut into S equal K ranges so that the pieces fill the chip, a 4-deep DMA ring so that
+// every CU keeps its weight stream in flight, fp32 partial tiles summed in K order by
+// splitk16_reduce_kernel (the next launch on the stream). The tokens are staged once per
+// slice for the 4 waves (the decode kernel's waves each reload them from L2).
+//
 // Operand staging as in gemm_dtl_kernel: K slices of 64 by LDS DMA into a ring of
-// STAGES buffers, each operand's rows dealt to whole waves; a wave whose operand runs
-// out of rows issues its remaining DMAs past the operand's bounds, where the buffer
+// STAGES buffers; the weight rows are dealt to the first W0 waves, the token rows to
+// the others, each wave an equal run of whole DMA rows. A wave whose run is shorter than
+// its IPW instructions issues the rest past the operand's bounds, where the buffer
 // descriptor's range check drops them, so every wave waits on the same counts.
 //
 // MFMA 16x16x32 operand mapping (lane l, l16 = l % 16, lq = l / 16):
 //   A: lane l holds W[n0 + l16][k0 + 8*lq .. +7];  B: lane l holds X[m0 + l16][k0 + 8*lq .. +7]
 //   D: register e of lane l holds D[n0 + 4*lq + e][m0 + l16]
 // ---------------------------------------------------------------------------------
-template <int TN, int TM>
+template <int TN, int TM, bool SW = false>
 struct Dtl16Shape {
     static constexpr int NWAVES = 4, NT = 256;
     static constexpr int WN = TN / 2, WM = TM / 2;   // outputs per wave (2 x 2 waves)
-    static constexpr int NA = WN / 16, BM = WM / 16;  // 16-row blocks per wave
+    static constexpr int NA = WN / 16, BM = WM / 16;  // 16-row blocks per wave (of each weight operand)
+    static constexpr int NAT = SW ? 2 * NA : NA;      // A blocks per wave: gate blocks, then up blocks
+    static constexpr int NG = NAT * BM;               // float4 accumulator groups per thread
+    static constexpr int NOPW = SW ? 2 : 1;           // weight operands (SwiGLU: gate and up)
     static constexpr int ROWB = DBK * 2, CPR = DBK / 8, RPW = 256 / ROWB, RPI = 64 / CPR;
-    static constexpr int waves_for(int ipw) { return (TN + ipw * RPI - 1) / (ipw * RPI) + (TM + ipw * RPI - 1) / (ipw * RPI); }
+    // Rows per wave of an operand of r rows over w waves, or 0 when they do not split into
+    // whole DMA instructions that fit ipw.
+    static constexpr int run(int r, int w, int ipw) { return (r % w == 0 && (r / w) % RPI == 0 && r / w <= ipw * RPI) ? r / w : 0; }
+    static constexpr int fit(int ipw) {  // waves per weight operand for ipw instructions per wave, 0 if none fits
+        for (int w0 = 1; NOPW * w0 < NWAVES; ++w0)
+            if (run(TN, w0, ipw) && run(TM, NWAVES - NOPW * w0, ipw)) return w0;
+        return 0;
+    }
     static constexpr int ipw_min() {
-        int i = ((TN + TM) / RPI + NWAVES - 1) / NWAVES;
-        while (waves_for(i) > NWAVES) ++i;
+        int i = ((NOPW * TN + TM) / RPI + NWAVES - 1) / NWAVES;
+        while (fit(i) == 0) ++i;
         return i;
     }
     static constexpr int IPW = ipw_min();                  // DMA instructions per wave and slice
     static constexpr int RPWV = IPW * RPI;                 // LDS rows per wave
-    static constexpr int W0 = (TN + RPWV - 1) / RPWV;      // waves loading weight rows
-    static constexpr int XB = W0 * RPWV;                   // first LDS row of the tokens
+    static constexpr int W0 = fit(IPW);                    // waves loading each weight operand's rows
+    static constexpr int RW = TN / W0, RX = TM / (NWAVES - NOPW * W0);  // operand rows per wave
+    static constexpr int UPB = W0 * RPWV;                  // first LDS row of the up weights (SwiGLU)
+    static constexpr int XB = NOPW * W0 * RPWV;            // first LDS row of the tokens
     static constexpr int ROWS = NWAVES * RPWV;             // LDS rows per stage
-    static_assert(waves_for(IPW) == NWAVES, "the operands fill the waves");
-    static_assert(WN % 16 == 0 && WM % 16 == 0 && TN % RPI == 0 && TM % RPI == 0, "whole blocks and DMA rows");
+    static_assert(IPW < 32, "DMA instructions per wave");
+    static_assert(WN % 16 == 0 && WM % 16 == 0, "whole blocks");
 };
 
-template <int TN, int TM, int STAGES, bool BIAS, typename OutT>
+// The LDS row of operand row t of a tile: weight rows t in the first W0 waves' runs (the up
+// weights of the SwiGLU pair the same after UPB), token rows after XB.
+template <typename Sh>
+__device__ __forceinline__ int dtl16_wrow(int t) { return (t / Sh::RW) * Sh::RPWV + t % Sh::RW; }
+template <typename Sh>
+__device__ __forceinline__ int dtl16_xrow(int t) { return Sh::XB + (t / Sh::RX) * Sh::RPWV + t % Sh::RX; }
+
+template <int TN, int TM, int STAGES, int ACT, bool BIAS, bool SK, typename OutT>
 __global__ __launch_bounds__(256) void gemm_dtl16_kernel(GemmParams p) {
-    using Sh = Dtl16Shape<TN, TM>;
-    constexpr int NA = Sh::NA, BM = Sh::BM, WN = Sh::WN, WM = Sh::WM;
+    constexpr bool SW = ACT == kActSwiglu;
+    using Sh = Dtl16Shape<TN, TM, SW>;
+    constexpr int NA = Sh::NA, NAT = Sh::NAT, BM = Sh::BM, WN = Sh::WN, WM = Sh::WM, NT = Sh::NT;
     constexpr int ROWB = Sh::ROWB, CPR = Sh::CPR, RPW = Sh::RPW, RPI = Sh::RPI, IPW = Sh::IPW, RPWV = Sh::RPWV;
     constexpr int STAGEB = Sh::ROWS * ROWB;
     constexpr int KS = DBK / 32;  // MFMA sub-steps per slice
@@ -726,16 +754,29 @@ __global__ __launch_bounds__(256) void gemm_dtl16_kernel(GemmParams p) {
     const int wn = wave & 1, wm = wave >> 1;
     const int l16 = lane & 15, lq = lane >> 4;
 
-    int tn, tm;
-    tile_of(blockIdx.x, p.tiles_n, p.tiles_m, tn, tm);
+    // Tile and K range: one whole tile per workgroup, or (SK) piece q = K range sp of tile
+    // r, pieces side by side on one XCD holding neighbouring tiles at the same K range.
+    const int KTALL = p.K / DBK;
+    int tn, tm, kt0 = 0, KT = KTALL, q = 0;
+    if (SK) {
+        const int R = p.tiles_n * p.tiles_m;
+        q = xcd_major((int)blockIdx.x, R * p.S);
+        const int sp = q / R, r = q - sp * R;
+        kt0 = (int)((int64_t)sp * KTALL / p.S);
+        KT = (int)((int64_t)(sp + 1) * KTALL / p.S) - kt0;
+        tile_coords(r, p.tiles_n, p.tiles_m, tn, tm);
+    } else {
+        tile_of(blockIdx.x, p.tiles_n, p.tiles_m, tn, tm);
+    }
     const int n0 = tn * TN, m0 = tm * TM;
 
     // This wave's DMA rows: operand rows t0 + j*RPI + lane/CPR into LDS rows
     // wave*RPWV + j*RPI + lane/CPR; chunk c of LDS row r sits at c ^ ((r / RPW) % CPR).
-    const bool wop = wave < Sh::W0;
-    const int t0 = (wop ? wave : wave - Sh::W0) * RPWV;
-    const int orows = wop ? TN : TM;
-    const void* obase = wop ? (const void*)p.W0 : (const void*)p.X;
+    const bool wop = wave < Sh::NOPW * Sh::W0;
+    const bool wup = SW && wave >= Sh::W0 && wop;
+    const int orun = wop ? Sh::RW : Sh::RX;
+    const int t0 = (wop ? (wup ? wave - Sh::W0 : wave) : wave - Sh::NOPW * Sh::W0) * orun;
+    const void* obase = wop ? (wup ? (const void*)p.W1 : (const void*)p.W0) : (const void*)p.X;
     const int64_t obytes = wop ? (int64_t)p.N * p.K * 2 : (int64_t)(p.M - 1) * p.ldx * 2 + (int64_t)p.K * 2;
     uint32_t goff[IPW];
 #pragma unroll
@@ -744,37 +785,43 @@ __global__ __launch_bounds__(256) void gemm_dtl16_kernel(GemmParams p) {
         const int row = wave * RPWV + lr;
         const int c = (lane % CPR) ^ ((row / RPW) % CPR);
         const int t = t0 + lr;
-        if (t0 + j * RPI >= orows) {
-            goff[j] = (uint32_t)obytes;  // past the operand: dropped by the range check
+        if (j * RPI >= orun) {
+            goff[j] = (uint32_t)obytes;  // past the wave's run: dropped by the range check
         } else if (wop) {
             goff[j] = (uint32_t)(((int64_t)min(n0 + t, p.N - 1) * p.K + c * 8) * 2);
         } else {
             goff[j] = (uint32_t)(((int64_t)min(m0 + t, p.M - 1) * p.ldx + c * 8) * 2);
         }
     }
-    const int KT = p.K / DBK;
 
-    // Fragment reads: block i of this lane is LDS row wn*WN + 16 i + l16 (weights) or
-    // XB + wm*WM + 16 j + l16 (tokens); every block starts on a multiple of 16 rows, so the
-    // swizzle term is (l16 / RPW) % CPR for all of them. Sub-step ks takes chunk 4 ks + lq.
+    // Fragment reads: block i of this lane is weight row wn*WN + 16 i + l16 (SwiGLU: blocks
+    // NA + i the up rows of the same features) and block j token row wm*WM + 16 j + l16, at
+    // their LDS rows; every 16-row block lies in one wave's run
+    // and starts on a multiple of 16 LDS rows, so the swizzle term is (l16 / RPW) % CPR for
+    // all of them. Sub-step ks takes chunk 4 ks + lq.
+    static_assert(Sh::RW % 16 == 0 && Sh::RX % 16 == 0 && RPWV % 16 == 0, "16-row blocks stay in one run");
     const int sw = (l16 / RPW) % CPR;
-    const int abase = (wn * WN + l16) * ROWB;
-    const int bbase = (Sh::XB + wm * WM + l16) * ROWB;
-    floatx4 acc[NA][BM];
+    int arow[NAT], brow[BM];
 #pragma unroll
-    for (int i = 0; i < NA; ++i)
+    for (int i = 0; i < NAT; ++i)
+        arow[i] = ((i < NA ? 0 : Sh::UPB) + dtl16_wrow<Sh>(wn * WN + 16 * (i % NA) + l16)) * ROWB;
+#pragma unroll
+    for (int j = 0; j < BM; ++j) brow[j] = dtl16_xrow<Sh>(wm * WM + 16 * j + l16) * ROWB;
+    floatx4 acc[NAT][BM];
+#pragma unroll
+    for (int i = 0; i < NAT; ++i)
 #pragma unroll
         for (int j = 0; j < BM; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-    auto read_frags = [&](const char* s, int ks, bf16x8 (&af)[NA], bf16x8 (&bfr)[BM]) {
+    auto read_frags = [&](const char* s, int ks, bf16x8 (&af)[NAT], bf16x8 (&bfr)[BM]) {
         const int kx = ((4 * ks + lq) ^ sw) * 16;
 #pragma unroll
-        for (int i = 0; i < NA; ++i) af[i] = *reinterpret_cast<const bf16x8*>(s + abase + i * 16 * ROWB + kx);
+        for (int i = 0; i < NAT; ++i) af[i] = *reinterpret_cast<const bf16x8*>(s + arow[i] + kx);
 #pragma unroll
-        for (int j = 0; j < BM; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(s + bbase + j * 16 * ROWB + kx);
+        for (int j = 0; j < BM; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(s + brow[j] + kx);
     };
-    auto mfmas = [&](bf16x8 (&af)[NA], bf16x8 (&bfr)[BM]) {
+    auto mfmas = [&](bf16x8 (&af)[NAT], bf16x8 (&bfr)[BM]) {
 #pragma unroll
-        for (int i = 0; i < NA; ++i)
+        for (int i = 0; i < NAT; ++i)
 #pragma unroll
             for (int j = 0; j < BM; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
@@ -789,13 +836,14 @@ __global__ __launch_bounds__(256) void gemm_dtl16_kernel(GemmParams p) {
         __builtin_amdgcn_s_barrier();
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
     };
-    constexpr int NMF = NA * BM, NRD = NA + BM;
-    static_assert(NRD + IPW <= NMF, "every read and DMA of sub-step 0 follows an MFMA");
-    bf16x8 fa0[NA], fb0[BM], fa1[NA], fb1[BM];
+    constexpr int NMF = NAT * BM, NRD = NAT + BM;
+    static_assert(NRD <= NMF, "every fragment read follows an MFMA");
+    constexpr int DTAIL = NRD + IPW > NMF ? NRD + IPW - NMF : 0;  // refill DMAs behind the last MFMA
+    bf16x8 fa0[NAT], fb0[BM], fa1[NAT], fb1[BM];
 
     // Prologue: every buffer requested; sub-step 0 of the first slice read.
     for (int st = 0; st < STAGES && st < KT; ++st)
-        dma_rows<IPW>(obase, (uint32_t)obytes, goff, (uint32_t)(st * DBK * 2), &lds[st][wave * RPWV * ROWB]);
+        dma_rows<IPW>(obase, (uint32_t)obytes, goff, (uint32_t)((kt0 + st) * DBK * 2), &lds[st][wave * RPWV * ROWB]);
     sync_slice(min(KT - 1, STAGES - 1));
     read_frags(lds[0], 0, fa0, fb0);
     __builtin_amdgcn_s_waitcnt(kLgkm0);
@@ -807,7 +855,7 @@ __global__ __launch_bounds__(256) void gemm_dtl16_kernel(GemmParams p) {
         const char* s = lds[kt % STAGES];
         read_frags(s, 1, fa1, fb1);
         if (REFILL)
-            dma_rows<IPW>(obase, (uint32_t)obytes, goff, (uint32_t)((kt - 1 + STAGES) * DBK * 2),
+            dma_rows<IPW>(obase, (uint32_t)obytes, goff, (uint32_t)((kt0 + kt - 1 + STAGES) * DBK * 2),
                           &lds[(kt + STAGES - 1) % STAGES][wave * RPWV * ROWB]);
         mfmas(fa0, fb0);
 #pragma unroll
@@ -816,6 +864,7 @@ __global__ __launch_bounds__(256) void gemm_dtl16_kernel(GemmParams p) {
             if (q < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
             else if (REFILL && q - NRD < IPW) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one DMA
         }
+        if (REFILL && DTAIL > 0) __builtin_amdgcn_sched_group_barrier(0x020, DTAIL, 0);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(kLgkm0);
         // On the last slice this synchronises once more and reads a buffer nobody uses any
@@ -837,45 +886,105 @@ __global__ __launch_bounds__(256) void gemm_dtl16_kernel(GemmParams p) {
     for (; kt + STAGES - 1 < KT; ++kt) slice(kt, std::true_type{});
     for (; kt < KT; ++kt) slice(kt, std::false_type{});
 
+    if (SK) {
+        // The fp32 partial tile as float4 groups [group][thread], every store contiguous.
+        floatx4* dst = reinterpret_cast<floatx4*>(p.ws) + (int64_t)q * Sh::NG * NT + tid;
+#pragma unroll
+        for (int i = 0; i < NAT; ++i)
+#pragma unroll
+            for (int j = 0; j < BM; ++j) dst[(i * BM + j) * NT] = acc[i][j];
+        return;
+    }
     // Epilogue: register e of block (i, j) holds feature wn*WN + 16 i + 4 lq + e of token
-    // wm*WM + 16 j + l16; bias, one rounding, 4 consecutive outputs per store.
+    // wm*WM + 16 j + l16 (SwiGLU: its up sum in block (NA + i, j)); bias, activation, one
+    // rounding, 4 consecutive outputs per store.
 #pragma unroll
     for (int i = 0; i < NA; ++i)
 #pragma unroll
         for (int j = 0; j < BM; ++j) {
             float gv[4], uv[4] = {};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) gv[e] = acc[i][j][e];
+            for (int e = 0; e < 4; ++e) {
+                gv[e] = acc[i][j][e];
+                if (SW) uv[e] = acc[(i + NA) % NAT][j][e];
+            }
             const int n_base = n0 + wn * WN + 16 * i + 4 * lq;
             const int m = m0 + wm * WM + 16 * j + l16;
-            epilogue4<kActNone, BIAS, OutT>(p.o, n_base, m, gv, uv);
+            epilogue4<ACT, BIAS, OutT>(p.o, n_base, m, gv, uv);
             __builtin_amdgcn_sched_barrier(0);
         }
 }
 
-template <int TN, int TM, bool BIAS, typename OutT>
-tp_status_t run_dtl16(const LinearDesc& d, const Ctx& c) {
-    if (c.planning()) return TP_OK;  // no work space
+// The S pieces of every tile of gemm_dtl16_kernel<SK>, summed in K order, then the
+// epilogue. Workgroup (r, g) takes float4 group g of every thread of tile r, so thread
+// tid reads exactly the group it would have held; S is a compile-time count so that
+// every piece's load is in flight before the first add.
+template <int TN, int TM, int ACT, bool BIAS, typename OutT, int S>
+__global__ __launch_bounds__(256) void splitk16_reduce_kernel(GemmParams p) {
+    constexpr bool SW = ACT == kActSwiglu;
+    using Sh = Dtl16Shape<TN, TM, SW>;
+    constexpr int NT = Sh::NT, NG = Sh::NG, BM = Sh::BM, NA = Sh::NA;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wn = wave & 1, wm = wave >> 1;
+    const int l16 = lane & 15, lq = lane >> 4;
+    const int R = p.tiles_n * p.tiles_m;
+    // Workgroup (r, g), g < NA * BM: the output group (i, j) (SwiGLU: with its up group
+    // (NA + i, j)).
+    const int g = (int)blockIdx.x % (NA * BM), r = (int)blockIdx.x / (NA * BM);
+    const int i = g / BM, j = g % BM;
+    int tn, tm;
+    tile_coords(r, p.tiles_n, p.tiles_m, tn, tm);
+    const floatx4* src = reinterpret_cast<const floatx4*>(p.ws) + (int64_t)r * NG * NT + tid;
+    const int64_t piece = (int64_t)R * NG * NT;  // float4s between pieces of one tile
+    constexpr int NS = SW ? 2 : 1;
+    floatx4 x[NS][S];
+#pragma unroll
+    for (int h = 0; h < NS; ++h)
+#pragma unroll
+        for (int sp = 0; sp < S; ++sp) x[h][sp] = src[sp * piece + (int64_t)((h * NA + i) * BM + j) * NT];
+    float gv[4], uv[4] = {};
+#pragma unroll
+    for (int h = 0; h < NS; ++h) {
+        floatx4 s = x[h][0];
+#pragma unroll
+        for (int sp = 1; sp < S; ++sp) s += x[h][sp];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) (h == 0 ? gv : uv)[e] = s[e];
+    }
+    const int n_base = tn * TN + wn * Sh::WN + 16 * i + 4 * lq;
+    const int m = tm * TM + wm * Sh::WM + 16 * j + l16;
+    epilogue4<ACT, BIAS, OutT>(p.o, n_base, m, gv, uv);
+}
+
+GemmParams dtl16_params(const LinearDesc& d, int TN, int TM, bool vec_store, bool vec16) {
     GemmParams p{};
     p.X = static_cast<const bf16*>(d.X);
     p.ldx = d.ldx;
     p.W0 = static_cast<const bf16*>(d.W0);
-    p.W1 = nullptr;
+    p.W1 = static_cast<const bf16*>(d.W1);
     p.o.Y = d.Y;
     p.o.ldy = d.ldy;
     p.o.M = (int)d.M;
     p.o.N = (int)d.N;
     p.o.b0 = static_cast<const bf16*>(d.b0);
-    p.o.b1 = nullptr;
-    p.o.vec_store = vec_store_ok<OutT>(d.Y, d.ldy);
-    p.o.vec16 = vec16_ok<OutT>(d.Y, d.ldy);
+    p.o.b1 = static_cast<const bf16*>(d.b1);
+    p.o.vec_store = vec_store;
+    p.o.vec16 = vec16;
     p.M = (int)d.M;
     p.N = (int)d.N;
     p.K = (int)d.K;
     p.tiles_n = (int)ceil_div(d.N, TN);
     p.tiles_m = (int)ceil_div(d.M, TM);
+    return p;
+}
+
+template <int TN, int TM, bool BIAS, typename OutT>
+tp_status_t run_dtl16(const LinearDesc& d, const Ctx& c) {
+    if (c.planning()) return TP_OK;  // no work space
+    GemmParams p = dtl16_params(d, TN, TM, vec_store_ok<OutT>(d.Y, d.ldy), vec16_ok<OutT>(d.Y, d.ldy));
     const int64_t tiles = (int64_t)p.tiles_n * p.tiles_m;
-    hipLaunchKernelGGL((gemm_dtl16_kernel<TN, TM, 3, BIAS, OutT>), dim3((unsigned)tiles), dim3(256), 0, c.stream, p);
+    hipLaunchKernelGGL((gemm_dtl16_kernel<TN, TM, 3, kActNone, BIAS, false, OutT>), dim3((unsigned)tiles), dim3(256),
+                       0, c.stream, p);
     return hip_status();
 }
 
@@ -885,6 +994,64 @@ tp_status_t run_dtl16_bias(const LinearDesc& d, const Ctx& c) {
     if (d.out_dtype == TP_DTYPE_BF16)
         return bias ? run_dtl16<TN, TM, true, bf16>(d, c) : run_dtl16<TN, TM, false, bf16>(d, c);
     return bias ? run_dtl16<TN, TM, true, float>(d, c) : run_dtl16<TN, TM, false, float>(d, c);
+}
+
+// Up to 64 tokens: every tile cut into S K ranges (S pieces per tile fill at most one wave of
+// CUs, each at least 4 slices), then the reduce pass.
+template <int TN, int TM, int ACT, bool BIAS, typename OutT, int S>
+tp_status_t run_dtl16_split_s(GemmParams p, int64_t tiles, const Ctx& c) {
+    using Sh = Dtl16Shape<TN, TM, ACT == kActSwiglu>;
+    hipLaunchKernelGGL((gemm_dtl16_kernel<TN, TM, 4, ACT, BIAS, true, OutT>), dim3((unsigned)(tiles * S)), dim3(256), 0,
+                       c.stream, p);
+    const tp_status_t st = hip_status();
+    if (st != TP_OK) return st;
+    hipLaunchKernelGGL((splitk16_reduce_kernel<TN, TM, ACT, BIAS, OutT, S>), dim3((unsigned)(tiles * Sh::NA * Sh::BM)),
+                       dim3(256), 0, c.stream, p);
+    return hip_status();
+}
+
+template <int TN, int TM, int ACT, bool BIAS, typename OutT>
+tp_status_t run_dtl16_split(const LinearDesc& d, int cus, const Ctx& c) {
+    GemmParams p = dtl16_params(d, TN, TM, vec_store_ok<OutT>(d.Y, d.ldy), vec16_ok<OutT>(d.Y, d.ldy));
+    const int64_t tiles = (int64_t)p.tiles_n * p.tiles_m;
+    const int64_t kt = d.K / DBK;
+    const int S = (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)cus / tiles, kt / 4, 16}));
+    const WsNeed need{(size_t)(tiles * S * Dtl16Shape<TN, TM, ACT == kActSwiglu>::NG * 1024), 0};
+    if (c.planning()) {
+        c.need->merge(need);
+        return TP_OK;
+    }
+    if (!c.ws || !c.ws->covers(need)) return TP_ERR_WORKSPACE;
+    p.S = S;
+    p.ws = c.ws->partials;
+    switch (S) {
+        case 1: return run_dtl16_split_s<TN, TM, ACT, BIAS, OutT, 1>(p, tiles, c);
+        case 2: return run_dtl16_split_s<TN, TM, ACT, BIAS, OutT, 2>(p, tiles, c);
+        case 3: return run_dtl16_split_s<TN, TM, ACT, BIAS, OutT, 3>(p, tiles, c);
+        case 4: return run_dtl16_split_s<TN, TM, ACT, BIAS, OutT, 4>(p, tiles, c);
+        case 5: return run_dtl16_split_s<TN, TM, ACT, BIAS, OutT, 5>(p, tiles, c);
+        case 6: return run_dtl16_split_s<TN, TM, ACT, BIAS, OutT, 6>(p, tiles, c);
+        case 7: return run_dtl16_split_s<TN, TM, ACT, BIAS, OutT, 7>(p, tiles, c);
+        case 8: return run_dtl16_split_s<TN, TM, ACT, BIAS, OutT, 8>(p, tiles, c);
+        case 9: return run_dtl16_split_s<TN, TM, ACT, BIAS, OutT, 9>(p, tiles, c);
+        case 10: return run_dtl16_split_s<TN, TM, ACT, BIAS, OutT, 10>(p, tiles, c);
+        case 11: return run_dtl16_split_s<TN, TM, ACT, BIAS, OutT, 11>(p, tiles, c);
+        case 12: return run_dtl16_split_s<TN, TM, ACT, BIAS, OutT, 12>(p, tiles, c);
+        case 13: return run_dtl16_split_s<TN, TM, ACT, BIAS, OutT, 13>(p, tiles, c);
+        case 14: return run_dtl16_split_s<TN, TM, ACT, BIAS, OutT, 14>(p, tiles, c);
+        case 15: return run_dtl16_split_s<TN, TM, ACT, BIAS, OutT, 15>(p, tiles, c);
+        default: return run_dtl16_split_s<TN, TM, ACT, BIAS, OutT, 16>(p, tiles, c);
+    }
+}
+
+template <int TN, int TM, int ACT>
+tp_status_t run_dtl16_split_bias(const LinearDesc& d, int cus, const Ctx& c) {
+    const bool bias = d.b0 != nullptr;
+    if (d.out_dtype == TP_DTYPE_BF16)
+        return bias ? run_dtl16_split<TN, TM, ACT, true, bf16>(d, cus, c)
+                    : run_dtl16_split<TN, TM, ACT, false, bf16>(d, cus, c);
+    return bias ? run_dtl16_split<TN, TM, ACT, true, float>(d, cus, c)
+                : run_dtl16_split<TN, TM, ACT, false, float>(d, cus, c);
 }
 
 template <int TN, int TM, int WAVES_N, int WAVES_M, int ACT, bool BIAS, typename OutT>
@@ -1060,6 +1227,13 @@ tp_status_t launch_gemm(const LinearDesc& d, const Ctx& c) {
     // 128 x 128 tiles.
     const bool dma = d.K % DBK == 0;
     const int64_t kt = d.K / DBK;
+    // 33-64 tokens (K a whole number of slices): one 64-token tile of 128 features (SwiGLU:
+    // 64 pairs) per piece, K cut so that the pieces fill the chip.
+    if (d.M <= 64) {
+        if (d.gelu || !dma) return TP_ERR_SHAPE;  // routed to the decode kernels
+        if (d.swiglu) return run_dtl16_split_bias<64, 64, kActSwiglu>(d, cus, c);
+        return run_dtl16_split_bias<128, 64, kActNone>(d, cus, c);
+    }
     if (d.swiglu) {
         const int64_t big = ceil_div(d.N, 128) * ceil_div(d.M, 256);
         if (dma && (big >= cus || big * kt >= 16 * (int64_t)cus))
