@@ -680,7 +680,7 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void splitk_reduce_kernel(Ge
 // can be 160 features x 128 tokens: 256 tiles, one per CU, each over the whole K, with
 // 80 x 64 outputs per wave (5 x 4 blocks: 9 fragment reads per 20 MFMAs).
 //
-// The same kernel takes 33-64 tokens as one 64-token tile (SK): 128-feature tiles, each
+// The same kernel takes up to 64 tokens as one 64-token tile (SK): 128-feature tiles, each
 // cut into S equal K ranges so that the pieces fill the chip, a 4-deep DMA ring so that
 // every CU keeps its weight stream in flight, fp32 partial tiles summed in K order by
 // splitk16_reduce_kernel (the next launch on the stream). The tokens are staged once per
@@ -1227,8 +1227,9 @@ tp_status_t launch_gemm(const LinearDesc& d, const Ctx& c) {
     // 128 x 128 tiles.
     const bool dma = d.K % DBK == 0;
     const int64_t kt = d.K / DBK;
-    // 33-64 tokens (K a whole number of slices): one 64-token tile of 128 features (SwiGLU:
-    // 64 pairs) per piece, K cut so that the pieces fill the chip.
+    // Up to 64 tokens (K a whole number of slices; the dispatcher sends 17-64 for the SwiGLU
+    // pair, 21-64 for plain products): one 64-token tile of 128 features (SwiGLU: 64 pairs)
+    // per piece, K cut so that the pieces fill the chip.
     if (d.M <= 64) {
         if (d.gelu || !dma) return TP_ERR_SHAPE;  // routed to the decode kernels
         if (d.swiglu) return run_dtl16_split_bias<64, 64, kActSwiglu>(d, cus, c);

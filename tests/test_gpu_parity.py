@@ -439,16 +439,18 @@ def test_dtl16_tiles(M, K, N, bias, f32):
     assert canaries_intact(buf, (M, N))
 
 
-# 33-64 tokens of a plain product (K a multiple of 64): one 64-token tile of 128 features per
-# piece on 16-row MFMA blocks, each tile's K cut into S ranges (S = 8 for the 7B TP=2 down shard,
-# 4 for the 70B TP=4 one, 2 and 1 below), fp32 partials summed in K order by the reduce pass.
+# 21-64 tokens of a plain product (K >= 2048, a multiple of 64): one 64-token tile of 128 features per
+# piece on 16-row MFMA blocks, each tile's K cut into S ranges (S = 8 for the 7B TP=2 down shard
+# and for 3 tiles, 4 for the 70B TP=4 one, 2 for 100 tiles, 1 for 157), fp32 partials summed in K
+# order by the reduce pass.
 @pytest.mark.parametrize("M,K,N,bias,f32", [(64, 5504, 4096, False, False), (64, 7168, 8192, False, True),
-                                            (40, 512, 1000, True, False), (33, 64, 300, True, False),
+                                            (40, 2048, 12800, True, False), (33, 2048, 300, True, False),
                                             (50, 4096, 20000, False, False), (48, 2048, 1300, False, True),
-                                            (48, 2048, 1300, True, False)])
+                                            (48, 2048, 1300, True, False), (21, 4096, 3000, True, False),
+                                            (32, 7168, 8192, False, True)])
 def test_dtl16_decode_split(M, K, N, bias, f32):
     assert not (bias and f32), "the row partial has no bias"
-    log_case("33-64 tokens on 16-row MFMA blocks, split K", M, K, N, bias, f32)
+    log_case("21-64 tokens on 16-row MFMA blocks, split K", M, K, N, bias, f32)
     x, w = I.activations(M, K, 371), I.weight(N, K, 372)
     b = I.bias(N, 373) if bias else None
     buf, Y = canary_buffer((M, N), torch.float32 if f32 else torch.bfloat16)
@@ -470,13 +472,14 @@ def test_dtl16_decode_split(M, K, N, bias, f32):
     assert torch.equal(Y, Y2)
 
 
-# The SwiGLU pair on the same path: 64 pairs x 64 tokens per piece, gate and up blocks of the
+# The SwiGLU pair on the same path (17-64 tokens): 64 pairs x 64 tokens per piece, gate and up blocks of the
 # same pairs in every wave (the 7B TP=2 and 70B TP=4 gate/up shards at 64 tokens, ragged pairs,
 # one K range when the tiles alone fill the chip).
 @pytest.mark.parametrize("M,K,I_,bias", [(64, 4096, 5504, False), (64, 8192, 7168, True), (33, 2048, 1000, True),
-                                         (48, 4096, 3000, False), (60, 2048, 20000, True)])
+                                         (48, 4096, 3000, False), (60, 2048, 20000, True), (17, 8192, 7168, False),
+                                         (24, 4096, 5504, True)])
 def test_dtl16_decode_swiglu(M, K, I_, bias):
-    log_case("33-64 tokens SwiGLU on 16-row MFMA blocks, split K", M, K, I_, bias)
+    log_case("17-64 tokens SwiGLU on 16-row MFMA blocks, split K", M, K, I_, bias)
     x = I.activations(M, K, 381)
     wg, wu = I.weight(I_, K, 382), I.weight(I_, K, 383)
     bg, bu = (I.bias(I_, 384), I.bias(I_, 385)) if bias else (None, None)
