@@ -678,7 +678,8 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void splitk_reduce_kernel(Ge
 // whole waves of CUs: the 70B TP=8 QKV shard (1280 features x 4096 tokens) has 80 such
 // tiles, which run as split-K pieces plus a reduce pass. With 16-row blocks the tile
 // can be 160 features x 128 tokens: 256 tiles, one per CU, each over the whole K, with
-// 80 x 64 outputs per wave (5 x 4 blocks: 9 fragment reads per 20 MFMAs).
+// 80 x 64 outputs per wave (5 x 4 blocks: 9 fragment reads per 20 MFMAs). With weights cold
+// from HBM it runs 90.6 us against 93.4 us for the split-K pieces and their reduce.
 //
 // The same kernel takes up to 64 tokens as one 64-token tile (SK): 128-feature tiles, each
 // cut into S equal K ranges so that the pieces fill the chip, a 4-deep DMA ring so that
@@ -983,7 +984,9 @@ tp_status_t run_dtl16(const LinearDesc& d, const Ctx& c) {
     if (c.planning()) return TP_OK;  // no work space
     GemmParams p = dtl16_params(d, TN, TM, vec_store_ok<OutT>(d.Y, d.ldy), vec16_ok<OutT>(d.Y, d.ldy));
     const int64_t tiles = (int64_t)p.tiles_n * p.tiles_m;
-    hipLaunchKernelGGL((gemm_dtl16_kernel<TN, TM, 3, kActNone, BIAS, false, OutT>), dim3((unsigned)tiles), dim3(256),
+    // A 4-deep ring (4 x 40 KB, all of a CU's LDS): with the weights cold from HBM, as in the
+    // layer, the QKV shard at 4096 tokens takes 90.6 us against 96.8 us with 3 buffers.
+    hipLaunchKernelGGL((gemm_dtl16_kernel<TN, TM, 4, kActNone, BIAS, false, OutT>), dim3((unsigned)tiles), dim3(256),
                        0, c.stream, p);
     return hip_status();
 }
