@@ -1000,7 +1000,7 @@ tp_status_t run_dtl16_bias(const LinearDesc& d, const Ctx& c) {
 }
 
 // Up to 64 tokens: every tile cut into S K ranges (S pieces per tile fill at most one wave of
-// CUs, each at least 4 slices), then the reduce pass.
+// CUs, each at least 4 slices, S <= 16), then the reduce pass; S = 1 runs whole tiles.
 template <int TN, int TM, int ACT, bool BIAS, typename OutT, int S>
 tp_status_t run_dtl16_split_s(GemmParams p, int64_t tiles, const Ctx& c) {
     using Sh = Dtl16Shape<TN, TM, ACT == kActSwiglu>;
@@ -1019,6 +1019,13 @@ tp_status_t run_dtl16_split(const LinearDesc& d, int cus, const Ctx& c) {
     const int64_t tiles = (int64_t)p.tiles_n * p.tiles_m;
     const int64_t kt = d.K / DBK;
     const int S = (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)cus / tiles, kt / 4, 16}));
+    if (S == 1) {  // the tiles alone fill the chip: whole K per workgroup, no partials
+        if (c.planning()) return TP_OK;
+        hipLaunchKernelGGL((gemm_dtl16_kernel<TN, TM, 4, ACT, BIAS, false, OutT>), dim3((unsigned)tiles), dim3(256), 0,
+                           c.stream, p);
+        return hip_status();
+    }
+    // S > 1 only when tiles * S <= cus: at most cus fp32 partial tiles.
     const WsNeed need{(size_t)(tiles * S * Dtl16Shape<TN, TM, ACT == kActSwiglu>::NG * 1024), 0};
     if (c.planning()) {
         c.need->merge(need);
@@ -1028,7 +1035,6 @@ tp_status_t run_dtl16_split(const LinearDesc& d, int cus, const Ctx& c) {
     p.S = S;
     p.ws = c.ws->partials;
     switch (S) {
-        case 1: return run_dtl16_split_s<TN, TM, ACT, BIAS, OutT, 1>(p, tiles, c);
         case 2: return run_dtl16_split_s<TN, TM, ACT, BIAS, OutT, 2>(p, tiles, c);
         case 3: return run_dtl16_split_s<TN, TM, ACT, BIAS, OutT, 3>(p, tiles, c);
         case 4: return run_dtl16_split_s<TN, TM, ACT, BIAS, OutT, 4>(p, tiles, c);
