@@ -525,7 +525,8 @@ def attnproj_bench(iters=100):
             rec = {"workload": shape.name, "M": M, "op": op, "us": round(us, 2), "us_back_to_back": round(us_b2b, 2),
                    "GB_s": round(by / us / 1e3, 1), "TFLOP_s": round(fl / us / 1e6, 2)}
             if M <= 64:
-                rec["kernel"] = "skinny_kernel"
+                # at one token the QKV shard's 80 row groups of 16 take the GEMV kernel (fewer than CUs)
+                rec["kernel"] = "gemv_kernel" if op == "qkv_col" else "skinny_kernel"
                 rec["hbm_frac"] = round(by / us / 1e3 / HBM_PEAK_GBS, 3)
                 rec["hbm_frac_back_to_back"] = round(by / us_b2b / 1e3 / HBM_PEAK_GBS, 3)
             else:
