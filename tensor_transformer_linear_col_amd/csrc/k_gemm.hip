@@ -272,6 +272,22 @@ constexpr unsigned vmcnt_wait(int n) {  // s_waitcnt immediate: vmcnt(n), no oth
 }
 constexpr unsigned kLgkm0 = 0xC07F;     // s_waitcnt immediate: lgkmcnt(0) only
 
+// Wait until at most min(ahead, A) * IPW of this wave's vector memory instructions are in
+// flight (the DMAs of the slices requested after the one needed next).
+template <int IPW, int A>
+__device__ __forceinline__ void wait_ahead(int ahead) {
+    if constexpr (A > 0) {
+        static_assert(A * IPW < 64, "vmcnt has 6 bits");
+        if (ahead >= A) {
+            __builtin_amdgcn_s_waitcnt(vmcnt_wait(A * IPW));
+            return;
+        }
+        wait_ahead<IPW, A - 1>(ahead);
+    } else {
+        __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+    }
+}
+
 // One wave's DMA of a stage: IPW instructions of 1 KB each into consecutive LDS
 // blocks, through a raw buffer descriptor of the operand (bounds = its byte size).
 // The descriptor type exists only for the GPU target, so the body is compiled in
@@ -828,18 +844,15 @@ __global__ __launch_bounds__(256) void gemm_dtl16_kernel(GemmParams p) {
                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     };
     auto sync_slice = [&](int ahead) {
-        static_assert(STAGES <= 4, "waits below cover up to 3 slices ahead");
-        if (ahead >= 3) __builtin_amdgcn_s_waitcnt(vmcnt_wait(3 * IPW));
-        else if (ahead == 2) __builtin_amdgcn_s_waitcnt(vmcnt_wait(2 * IPW));
-        else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vmcnt_wait(IPW));
-        else __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+        wait_ahead<IPW, STAGES - 1>(ahead);
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_s_barrier();
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
     };
     constexpr int NMF = NAT * BM, NRD = NAT + BM;
-    static_assert(NRD <= NMF, "every fragment read follows an MFMA");
-    constexpr int DTAIL = NRD + IPW > NMF ? NRD + IPW - NMF : 0;  // refill DMAs behind the last MFMA
+    // Reads and refill DMAs that find no MFMA to follow go behind the last one.
+    constexpr int RTAIL = NRD > NMF ? NRD - NMF : 0;
+    constexpr int DTAIL = NRD + IPW > NMF ? (NRD > NMF ? IPW : NRD + IPW - NMF) : 0;
     bf16x8 fa0[NAT], fb0[BM], fa1[NAT], fb1[BM];
 
     // Prologue: every buffer requested; sub-step 0 of the first slice read.
@@ -865,6 +878,7 @@ __global__ __launch_bounds__(256) void gemm_dtl16_kernel(GemmParams p) {
             if (q < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
             else if (REFILL && q - NRD < IPW) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one DMA
         }
+        if (RTAIL > 0) __builtin_amdgcn_sched_group_barrier(0x100, RTAIL, 0);
         if (REFILL && DTAIL > 0) __builtin_amdgcn_sched_group_barrier(0x020, DTAIL, 0);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(kLgkm0);
@@ -879,6 +893,7 @@ __global__ __launch_bounds__(256) void gemm_dtl16_kernel(GemmParams p) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             if (q < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
+        if (RTAIL > 0) __builtin_amdgcn_sched_group_barrier(0x100, RTAIL, 0);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(kLgkm0);
     };
@@ -999,12 +1014,22 @@ tp_status_t run_dtl16_bias(const LinearDesc& d, const Ctx& c) {
     return bias ? run_dtl16<TN, TM, true, float>(d, c) : run_dtl16<TN, TM, false, float>(d, c);
 }
 
+// Ring depth of the decode tiles: 4 slices of 32 KB (128 x 64 tiles, 64 SwiGLU pairs x 64;
+// a fifth measured no faster), else as many as the LDS holds, at most 10 (32 pairs x 64 tokens:
+// 10 x 16 KB).
+template <int TN, int TM, bool SW>
+constexpr int dtl16_decode_stages() {
+    constexpr int b = Dtl16Shape<TN, TM, SW>::ROWS * Dtl16Shape<TN, TM, SW>::ROWB;
+    return b >= 32 * 1024 ? 4 : ((160 * 1024) / b > 10 ? 10 : (160 * 1024) / b);
+}
+
 // Up to 64 tokens: every tile cut into S K ranges (S pieces per tile fill at most one wave of
 // CUs, each at least 4 slices, S <= 16), then the reduce pass; S = 1 runs whole tiles.
 template <int TN, int TM, int ACT, bool BIAS, typename OutT, int S>
 tp_status_t run_dtl16_split_s(GemmParams p, int64_t tiles, const Ctx& c) {
     using Sh = Dtl16Shape<TN, TM, ACT == kActSwiglu>;
-    hipLaunchKernelGGL((gemm_dtl16_kernel<TN, TM, 4, ACT, BIAS, true, OutT>), dim3((unsigned)(tiles * S)), dim3(256), 0,
+    constexpr int ST = dtl16_decode_stages<TN, TM, ACT == kActSwiglu>();
+    hipLaunchKernelGGL((gemm_dtl16_kernel<TN, TM, ST, ACT, BIAS, true, OutT>), dim3((unsigned)(tiles * S)), dim3(256), 0,
                        c.stream, p);
     const tp_status_t st = hip_status();
     if (st != TP_OK) return st;
@@ -1021,7 +1046,8 @@ tp_status_t run_dtl16_split(const LinearDesc& d, int cus, const Ctx& c) {
     const int S = (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)cus / tiles, kt / 4, 16}));
     if (S == 1) {  // the tiles alone fill the chip: whole K per workgroup, no partials
         if (c.planning()) return TP_OK;
-        hipLaunchKernelGGL((gemm_dtl16_kernel<TN, TM, 4, ACT, BIAS, false, OutT>), dim3((unsigned)tiles), dim3(256), 0,
+        constexpr int ST = dtl16_decode_stages<TN, TM, ACT == kActSwiglu>();
+        hipLaunchKernelGGL((gemm_dtl16_kernel<TN, TM, ST, ACT, BIAS, false, OutT>), dim3((unsigned)tiles), dim3(256), 0,
                            c.stream, p);
         return hip_status();
     }
@@ -1241,6 +1267,12 @@ tp_status_t launch_gemm(const LinearDesc& d, const Ctx& c) {
     // per piece, K cut so that the pieces fill the chip.
     if (d.M <= 64) {
         if (d.gelu || !dma) return TP_ERR_SHAPE;  // routed to the decode kernels
+        // Up to 48 tokens of a SwiGLU pair whose 32-pair tiles fill 80-100 % of the CUs: whole-K
+        // tiles of 32 pairs in a 10-deep ring, no partials (70B TP=4 gate/up at 32 tokens:
+        // 48.6 -> 45.2 us; at 64 tokens, and for plain products, no faster or slower).
+        const int64_t t32 = ceil_div(d.N, 32);
+        if (d.swiglu && d.M <= 48 && t32 * 10 >= (int64_t)cus * 8 && t32 <= cus)
+            return run_dtl16_split_bias<32, 64, kActSwiglu>(d, cus, c);
         if (d.swiglu) return run_dtl16_split_bias<64, 64, kActSwiglu>(d, cus, c);
         return run_dtl16_split_bias<128, 64, kActNone>(d, cus, c);
     }
