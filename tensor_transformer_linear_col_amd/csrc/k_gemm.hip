@@ -1236,17 +1236,35 @@ tp_status_t run_bias(const LinearDesc& d, const Ctx& c) {
 
 }  // namespace
 
+namespace {
+int device_cus() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+        return n;
+    return 256;
+}
+
+// A SwiGLU pair of up to 48 tokens whose 32-pair tiles fill 80-100 % of the CUs: whole-K
+// tiles of 32 pairs x 64 tokens in a 10-deep ring, no partials (70B TP=4 gate/up: 48.9 ->
+// 43.5 us at 8 tokens, 50.4 -> 43.7 at 4, 46.9 -> 43.7 at 16, 48.6 -> 45.2 at 32, equal at 1;
+// at 64 tokens, and for plain products, no faster or slower).
+bool swiglu_pairs32(const LinearDesc& d, int cus) {
+    const int64_t t32 = ceil_div(d.N, 32);
+    return d.swiglu && d.M <= 48 && t32 * 10 >= (int64_t)cus * 8 && t32 <= cus;
+}
+}  // namespace
+
+bool gemm_takes_decode(const LinearDesc& d) {
+    if (d.M > 64 || d.gelu || d.K % DBK != 0 || d.K < 2048) return false;
+    return swiglu_pairs32(d, device_cus()) || d.M > (d.swiglu ? 16 : 20);
+}
+
 tp_status_t launch_gemm(const LinearDesc& d, const Ctx& c) {
     // Byte offsets inside an operand are 32-bit.
     if ((int64_t)d.N * d.K * 2 >= (int64_t(1) << 32) || (int64_t)d.M * d.ldx * 2 >= (int64_t(1) << 32))
         return TP_ERR_SHAPE;
-    int cus = 256;
-    {
-        int dev = 0, n = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-            cus = n;
-    }
+    const int cus = device_cus();
     // Large tiles (256 x 256, or 128 x 256 with the SwiGLU pair, one workgroup per CU)
     // when they fill the chip; with K a whole number of slices they run on the LDS-DMA
     // kernel with 8 waves of 128 x 64 outputs (SwiGLU: 16 waves of 32 pairs x 64), so a
@@ -1262,17 +1280,11 @@ tp_status_t launch_gemm(const LinearDesc& d, const Ctx& c) {
     // 128 x 128 tiles.
     const bool dma = d.K % DBK == 0;
     const int64_t kt = d.K / DBK;
-    // Up to 64 tokens (K a whole number of slices; the dispatcher sends 17-64 for the SwiGLU
-    // pair, 21-64 for plain products): one 64-token tile of 128 features (SwiGLU: 64 pairs)
-    // per piece, K cut so that the pieces fill the chip.
+    // Decode shapes that gemm_takes_decode accepts: 64-token tiles of 128 features (SwiGLU: 64
+    // pairs) per piece, K cut so that the pieces fill the chip, or whole-K tiles of 32 pairs.
     if (d.M <= 64) {
-        if (d.gelu || !dma) return TP_ERR_SHAPE;  // routed to the decode kernels
-        // Up to 48 tokens of a SwiGLU pair whose 32-pair tiles fill 80-100 % of the CUs: whole-K
-        // tiles of 32 pairs in a 10-deep ring, no partials (70B TP=4 gate/up at 32 tokens:
-        // 48.6 -> 45.2 us; at 64 tokens, and for plain products, no faster or slower).
-        const int64_t t32 = ceil_div(d.N, 32);
-        if (d.swiglu && d.M <= 48 && t32 * 10 >= (int64_t)cus * 8 && t32 <= cus)
-            return run_dtl16_split_bias<32, 64, kActSwiglu>(d, cus, c);
+        if (!gemm_takes_decode(d)) return TP_ERR_SHAPE;  // the decode kernels' shapes
+        if (swiglu_pairs32(d, cus)) return run_dtl16_split_bias<32, 64, kActSwiglu>(d, cus, c);
         if (d.swiglu) return run_dtl16_split_bias<64, 64, kActSwiglu>(d, cus, c);
         return run_dtl16_split_bias<128, 64, kActNone>(d, cus, c);
     }

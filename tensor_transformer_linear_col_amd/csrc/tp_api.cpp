@@ -41,11 +41,11 @@ tp_status_t launch_linear(const LinearDesc& d, const Ctx& c) {
     // the GEMV kernel splits the features one by one instead (70B QKV shard at TP=8 and one
     // token: 10.3 -> 8.4 us). With enough row groups the MFMA kernel stays faster.
     if (d.M <= 4 && gemv_chunks(d.K, nullptr) != 0 && ceil_div(d.N, 16) < gemv_cus()) return launch_gemv(d, c);
-    // 17-64 tokens of the SwiGLU pair, 21-64 of a plain product, K >= 2048: the tokens staged
-    // once per workgroup in LDS, shared by its waves, instead of reloaded by every wave of the
-    // decode kernel (70B TP=4 at 64 tokens: gate/up 64.4 -> 49.9 us, down 40.0 -> 28.6 us; at
-    // 32 tokens 52.8 -> 48.4 / 32.9 -> 27.5 us). Fewer tokens and short K stay there.
-    if (d.M > (d.swiglu ? 16 : 20) && d.M <= 64 && !d.gelu && d.K % 64 == 0 && d.K >= 2048) return launch_gemm(d, c);
+    // Decode shapes with the tokens staged once per workgroup in LDS, shared by its waves,
+    // instead of reloaded by every wave of the decode kernel (gemm_takes_decode: 17-64 tokens
+    // of a SwiGLU pair, 21-64 of a plain product, K >= 2048; 70B TP=4 at 64 tokens: gate/up
+    // 64.4 -> 49.9 us, down 40.0 -> 28.6 us). Fewer tokens and short K stay on the decode kernel.
+    if (d.M <= 64 && gemm_takes_decode(d)) return launch_gemm(d, c);
     if (d.M <= 64) return launch_skinny(d, c);
     return launch_gemm(d, c);
 }

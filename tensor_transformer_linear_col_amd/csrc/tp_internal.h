@@ -74,6 +74,10 @@ int gemv_chunks(int64_t K, int* kw_out);
 // Compute units of the current device (256 when it cannot be read).
 int gemv_cus();
 tp_status_t launch_gemm(const LinearDesc& d, const Ctx& c);
+// Decode shapes (M <= 64) that launch_gemm takes on LDS-staged tiles instead of the decode
+// kernels: 17-64 tokens of a SwiGLU pair, 21-64 of a plain product, K >= 2048 and a multiple
+// of 64; and SwiGLU pairs of up to 48 tokens with 32-pair tiles for 80-100 % of the CUs.
+bool gemm_takes_decode(const LinearDesc& d);
 tp_status_t launch_f32(const LinearDesc& d, const Ctx& c);
 // Head-local attention core: out[M, hq*d] (row stride lda) from qkv[M, (hq+2hk)*d] (row stride ldq).
 tp_status_t launch_attn_core(const void* qkv, int64_t ldq, void* out, int64_t lda, int64_t M, int hq, int hk, int d,
