@@ -1245,19 +1245,20 @@ int device_cus() {
     return 256;
 }
 
-// A SwiGLU pair of up to 48 tokens whose 32-pair tiles fill 80-100 % of the CUs: whole-K
-// tiles of 32 pairs x 64 tokens in a 10-deep ring, no partials (70B TP=4 gate/up: 48.9 ->
-// 43.5 us at 8 tokens, 50.4 -> 43.7 at 4, 46.9 -> 43.7 at 16, 48.6 -> 45.2 at 32, equal at 1;
-// at 64 tokens, and for plain products, no faster or slower).
+// A SwiGLU pair of 17-48 tokens whose 32-pair tiles fill 80-100 % of the CUs: whole-K tiles
+// of 32 pairs x 64 tokens in a 10-deep ring, no partials (70B TP=4 gate/up at 32 tokens: 52.9 ->
+// 48.2 us). At 64 tokens, and for plain products, no faster or slower. At 1-16 tokens the
+// gain depends on the box (4-16 tokens 5-12 % faster on one, equal on another, and at one token
+// 47.4 -> 50.0 us): the decode kernel keeps those.
 bool swiglu_pairs32(const LinearDesc& d, int cus) {
     const int64_t t32 = ceil_div(d.N, 32);
-    return d.swiglu && d.M <= 48 && t32 * 10 >= (int64_t)cus * 8 && t32 <= cus;
+    return d.swiglu && d.M > 16 && d.M <= 48 && t32 * 10 >= (int64_t)cus * 8 && t32 <= cus;
 }
 }  // namespace
 
 bool gemm_takes_decode(const LinearDesc& d) {
     if (d.M > 64 || d.gelu || d.K % DBK != 0 || d.K < 2048) return false;
-    return swiglu_pairs32(d, device_cus()) || d.M > (d.swiglu ? 16 : 20);
+    return d.M > (d.swiglu ? 16 : 20);
 }
 
 tp_status_t launch_gemm(const LinearDesc& d, const Ctx& c) {

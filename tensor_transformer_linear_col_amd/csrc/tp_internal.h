@@ -76,7 +76,7 @@ int gemv_cus();
 tp_status_t launch_gemm(const LinearDesc& d, const Ctx& c);
 // Decode shapes (M <= 64) that launch_gemm takes on LDS-staged tiles instead of the decode
 // kernels: 17-64 tokens of a SwiGLU pair, 21-64 of a plain product, K >= 2048 and a multiple
-// of 64; and SwiGLU pairs of up to 48 tokens with 32-pair tiles for 80-100 % of the CUs.
+// of 64.
 bool gemm_takes_decode(const LinearDesc& d);
 tp_status_t launch_f32(const LinearDesc& d, const Ctx& c);
 // Head-local attention core: out[M, hq*d] (row stride lda) from qkv[M, (hq+2hk)*d] (row stride ldq).

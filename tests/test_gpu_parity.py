@@ -474,8 +474,9 @@ def test_dtl16_decode_split(M, K, N, bias, f32):
 
 # The SwiGLU pair on the same path (17-64 tokens; fewer below): 64 pairs x 64 tokens per piece, gate and up blocks of the
 # same pairs in every wave (the 7B TP=2 and 70B TP=4 gate/up shards at 64 tokens, ragged pairs,
-# one K range when the tiles alone fill the chip); 1-48 tokens with 205-256 tiles of 32 pairs
-# (the 70B shard, 8000 or 6600 pairs), whole-K tiles of 32 pairs in a 10-deep ring.
+# one K range when the tiles alone fill the chip); 17-48 tokens with 205-256 tiles of 32 pairs
+# (the 70B shard, 8000 pairs), whole-K tiles of 32 pairs in a 10-deep ring; and the same shapes
+# below 17 tokens, which stay on the decode kernel.
 @pytest.mark.parametrize("M,K,I_,bias", [(64, 4096, 5504, False), (64, 8192, 7168, True), (33, 2048, 1000, True),
                                          (48, 4096, 3000, False), (60, 2048, 20000, True), (17, 8192, 7168, False),
                                          (24, 4096, 5504, True), (32, 8192, 7168, True), (48, 4096, 8000, False),
