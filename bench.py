@@ -530,7 +530,8 @@ def attnproj_bench(iters=100):
                 rec["hbm_frac"] = round(by / us / 1e3 / HBM_PEAK_GBS, 3)
                 rec["hbm_frac_back_to_back"] = round(by / us_b2b / 1e3 / HBM_PEAK_GBS, 3)
             else:
-                rec["kernel"] = "gemm_dtl_kernel" + (" + splitk_reduce_kernel" if op == "qkv_col" else "")
+                # 2048 tokens: QKV as 128 tiles of 160 x 128 in 2 K ranges + their reduce; O on 256 x 256 tiles
+                rec["kernel"] = ("gemm_dtl16_kernel + splitk16_reduce_kernel" if op == "qkv_col" else "gemm_dtl_kernel")
                 rec["bf16_frac"] = round(fl / us / 1e6 / BF16_PEAK_TFLOPS, 4)
                 rec["bf16_frac_back_to_back"] = round(fl / us_b2b / 1e6 / BF16_PEAK_TFLOPS, 4)
             out.append(rec)

@@ -236,10 +236,14 @@ def test_dry_run_sizes_the_split_reductions(L):
     """A dry run validates, enqueues nothing (no GPU here, so any launch would fail with
     TP_ERR_HIP) and reports the largest work space of the calls inside it. Without a device
     the library plans for 256 compute units, as on MI355X."""
-    # 70B QKV shard at TP = 8 and 2048 tokens: 5 x 8 = 40 tiles of 256 x 256 on 256 CUs, each
-    # cut into 6 K ranges -> 240 fp32 partial tiles of 256 KB.
-    qkv = lambda: L.tp_attn_proj_shard(P, P, 0, P, 0, 0, 0, 2048, 8192, 64, 8, 128, 8, BF16, BF16, None)
-    assert _plan(L, qkv) == (OK, 240 * 256 * 256 * 4, 0)
+    # 70B QKV shard at TP = 8 and 1024 tokens: 5 x 4 = 20 tiles of 256 x 256 on 256 CUs, each
+    # cut into 8 K ranges -> 160 fp32 partial tiles of 256 KB.
+    qkv = lambda: L.tp_attn_proj_shard(P, P, 0, P, 0, 0, 0, 1024, 8192, 64, 8, 128, 8, BF16, BF16, None)
+    assert _plan(L, qkv) == (OK, 160 * 256 * 256 * 4, 0)
+    # At 2048 tokens: 8 x 16 = 128 tiles of 160 x 128, each cut into 2 K ranges -> 256 partial
+    # tiles of 80 KB.
+    qkv2k = lambda: L.tp_attn_proj_shard(P, P, 0, P, 0, 0, 0, 2048, 8192, 64, 8, 128, 8, BF16, BF16, None)
+    assert _plan(L, qkv2k) == (OK, 256 * 160 * 128 * 4, 0)
     # At 4096 tokens its 8 x 32 = 256 tiles of 160 x 128 fill the chip: no split, no work space.
     qkv4k = lambda: L.tp_attn_proj_shard(P, P, 0, P, 0, 0, 0, 4096, 8192, 64, 8, 128, 8, BF16, BF16, None)
     assert _plan(L, qkv4k) == (OK, 0, 0)
@@ -257,7 +261,7 @@ def test_dry_run_sizes_the_split_reductions(L):
     assert _plan(L, lambda: col(L, M=0)) == (OK, 0, 0)
     # Several calls: the largest need of any of them.
     both = lambda: (qkv1(), qkv(), gateup())[-1]
-    assert _plan(L, both) == (OK, 240 * 256 * 256 * 4, 40)
+    assert _plan(L, both) == (OK, 160 * 256 * 256 * 4, 40)
     # Validation still applies inside a dry run.
     assert _plan(L, lambda: col(L, X=0))[0] == NULL
 
