@@ -1307,9 +1307,11 @@ tp_status_t launch_gemm(const LinearDesc& d, const Ctx& c) {
         if (dma && A == kActNone && big < cus && kt >= 32 && t16 >= cus &&
             t16 * 10 >= ceil_div(t16, (int64_t)cus) * cus * 9)
             return run_dtl16_bias<160, 128>(d, c);
-        // Half as many: each tile cut into 2 K ranges, summed by the reduce pass (70B TP=8 QKV at
-        // 2048 tokens: 61.2 -> 55.1 us, a third of the partials of 256 x 256 tiles in 6 ranges).
-        if (dma && A == kActNone && big < cus && kt >= 32 && 2 * t16 <= cus && 2 * t16 * 10 >= (int64_t)cus * 9)
+        // Fewer: each tile cut into the S K ranges (at most 16, each >= 4 slices) that fill the
+        // chip to 90 %, summed by the reduce pass; 70B TP=8 QKV shard against 256 x 256 tiles cut
+        // in K: 2048 tokens 61.2 -> 55.1 us (2 ranges), 1024 42.2 -> 33.0 (4), 512 38.0 -> 23.2 (8).
+        const int64_t s16 = std::max<int64_t>(1, std::min<int64_t>({(int64_t)cus / std::max<int64_t>(t16, 1), kt / 4, 16}));
+        if (dma && A == kActNone && big < cus && kt >= 32 && t16 < cus && t16 * s16 * 10 >= (int64_t)cus * 9)
             return run_dtl16_split_bias<160, 128, kActNone>(d, cus, c);
         if (dma && (big >= cus || big * kt >= 16 * (int64_t)cus || (kt >= 32 && big * kt >= 8 * (int64_t)cus) ||
                     (kt >= 64 && 2 * small <= cus)))

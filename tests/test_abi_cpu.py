@@ -236,14 +236,17 @@ def test_dry_run_sizes_the_split_reductions(L):
     """A dry run validates, enqueues nothing (no GPU here, so any launch would fail with
     TP_ERR_HIP) and reports the largest work space of the calls inside it. Without a device
     the library plans for 256 compute units, as on MI355X."""
-    # 70B QKV shard at TP = 8 and 1024 tokens: 5 x 4 = 20 tiles of 256 x 256 on 256 CUs, each
-    # cut into 8 K ranges -> 160 fp32 partial tiles of 256 KB.
-    qkv = lambda: L.tp_attn_proj_shard(P, P, 0, P, 0, 0, 0, 1024, 8192, 64, 8, 128, 8, BF16, BF16, None)
-    assert _plan(L, qkv) == (OK, 160 * 256 * 256 * 4, 0)
-    # At 2048 tokens: 8 x 16 = 128 tiles of 160 x 128, each cut into 2 K ranges -> 256 partial
-    # tiles of 80 KB.
-    qkv2k = lambda: L.tp_attn_proj_shard(P, P, 0, P, 0, 0, 0, 2048, 8192, 64, 8, 128, 8, BF16, BF16, None)
-    assert _plan(L, qkv2k) == (OK, 256 * 160 * 128 * 4, 0)
+    # A 1320-feature column shard at 1000 tokens, K = 16384: its 9 x 8 = 72 tiles of 160 x 128 in
+    # 3 K ranges would fill only 216 of 256 CUs, so 6 x 4 = 24 tiles of 256 x 256 run, each cut
+    # into 8 K ranges -> 192 fp32 partial tiles of 256 KB.
+    big = lambda: col(L, M=1000, K=16384, N=2640, p=2)
+    assert _plan(L, big) == (OK, 192 * 256 * 256 * 4, 0)
+    # 70B QKV shard at TP = 8 and 2048 tokens: 8 x 16 = 128 tiles of 160 x 128, each cut into 2 K
+    # ranges -> 256 partial tiles of 80 KB; at 1024 tokens 64 tiles in 4 ranges, the same.
+    qkv = lambda: L.tp_attn_proj_shard(P, P, 0, P, 0, 0, 0, 2048, 8192, 64, 8, 128, 8, BF16, BF16, None)
+    assert _plan(L, qkv) == (OK, 256 * 160 * 128 * 4, 0)
+    qkv1k = lambda: L.tp_attn_proj_shard(P, P, 0, P, 0, 0, 0, 1024, 8192, 64, 8, 128, 8, BF16, BF16, None)
+    assert _plan(L, qkv1k) == (OK, 256 * 160 * 128 * 4, 0)
     # At 4096 tokens its 8 x 32 = 256 tiles of 160 x 128 fill the chip: no split, no work space.
     qkv4k = lambda: L.tp_attn_proj_shard(P, P, 0, P, 0, 0, 0, 4096, 8192, 64, 8, 128, 8, BF16, BF16, None)
     assert _plan(L, qkv4k) == (OK, 0, 0)
@@ -260,8 +263,8 @@ def test_dry_run_sizes_the_split_reductions(L):
     assert _plan(L, gateup) == (OK, 0, 0)
     assert _plan(L, lambda: col(L, M=0)) == (OK, 0, 0)
     # Several calls: the largest need of any of them.
-    both = lambda: (qkv1(), qkv(), gateup())[-1]
-    assert _plan(L, both) == (OK, 160 * 256 * 256 * 4, 40)
+    both = lambda: (qkv1(), big(), qkv(), gateup())[-1]
+    assert _plan(L, both) == (OK, 192 * 256 * 256 * 4, 40)
     # Validation still applies inside a dry run.
     assert _plan(L, lambda: col(L, X=0))[0] == NULL
 

@@ -421,11 +421,14 @@ def test_dma_kernel_swiglu_tails(M, K, I_):
 
 # 160 x 128 tiles on 16-row MFMA blocks: plain products with fewer 256 x 256 tiles than CUs
 # whose 160 x 128 tiles fill whole waves (the 70B TP=8 QKV shard's 1280 x 4096 outputs are 256
-# tiles), or half a wave, cut into 2 K ranges (1280 x 2048); ragged features and tokens, bias or
-# none, bf16 output or an fp32 row partial.
+# tiles), or fewer, each cut into the K ranges that fill the chip (1280 x 2048: 2; 1280 x 1024: 4;
+# 1280 x 256: 16; 1270 x 768: 5); ragged features and tokens, bias or none, bf16 output or an fp32
+# row partial.
 @pytest.mark.parametrize("M,K,N,bias,f32", [(4096, 8192, 1280, True, False), (4000, 4096, 1250, True, False),
                                             (3900, 2048, 2552, False, False), (4096, 2048, 1280, False, True),
-                                            (2000, 4096, 1250, True, False), (2048, 2048, 1280, False, True)])
+                                            (2000, 4096, 1250, True, False), (2048, 2048, 1280, False, True),
+                                            (256, 8192, 1280, True, False), (768, 4096, 1270, False, False),
+                                            (512, 2048, 2560, True, False), (1024, 4096, 1280, False, True)])
 def test_dtl16_tiles(M, K, N, bias, f32):
     log_case("160x128 tiles on 16-row MFMA blocks", M, K, N, bias, f32)
     x, w = I.activations(M, K, 361), I.weight(N, K, 362)
