@@ -687,21 +687,24 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void splitk_reduce_kernel(Ge
 }
 
 // ---------------------------------------------------------------------------------
-// Plain products on 16-row MFMA blocks: v_mfma_f32_16x16x32_bf16, TN x TM tiles of 4
-// waves with (TN/2) x (TM/2) outputs each.
+// Products on 16-row MFMA blocks: v_mfma_f32_16x16x32_bf16, TN x TM tiles of 4 waves
+// with (TN/2) x (TM/2) outputs each (plain products; the SwiGLU pair at up to 64 tokens).
 //
 // 32-row blocks leave no good layout for a product whose 256 x 256 tiles do not fill
 // whole waves of CUs: the 70B TP=8 QKV shard (1280 features x 4096 tokens) has 80 such
 // tiles, which run as split-K pieces plus a reduce pass. With 16-row blocks the tile
 // can be 160 features x 128 tokens: 256 tiles, one per CU, each over the whole K, with
 // 80 x 64 outputs per wave (5 x 4 blocks: 9 fragment reads per 20 MFMAs). With weights cold
-// from HBM it runs 90.6 us against 93.4 us for the split-K pieces and their reduce.
+// from HBM it runs 90.6 us against 93.4 us for the split-K pieces and their reduce. With
+// fewer tokens the same tiles are cut into the S equal K ranges that fill the chip (SK):
+// fp32 partial tiles summed in K order by splitk16_reduce_kernel, the next launch on the
+// stream (2048 tokens: 2 ranges, a third of the partials of 256 x 256 tiles in 6).
 //
-// The same kernel takes up to 64 tokens as one 64-token tile (SK): 128-feature tiles, each
-// cut into S equal K ranges so that the pieces fill the chip, a 4-deep DMA ring so that
-// every CU keeps its weight stream in flight, fp32 partial tiles summed in K order by
-// splitk16_reduce_kernel (the next launch on the stream). The tokens are staged once per
-// slice for the 4 waves (the decode kernel's waves each reload them from L2).
+// The same kernel takes up to 64 tokens as one 64-token tile (SK): 128-feature tiles (64
+// SwiGLU pairs), each cut into K ranges the same way, a 4-deep DMA ring so that every CU
+// keeps its weight stream in flight; or whole-K tiles of 32 pairs in a 10-deep ring. The
+// tokens are staged once per slice for the 4 waves (the decode kernel's waves each reload
+// them from L2).
 //
 // Operand staging as in gemm_dtl_kernel: K slices of 64 by LDS DMA into a ring of
 // STAGES buffers; the weight rows are dealt to the first W0 waves, the token rows to
@@ -1274,11 +1277,12 @@ tp_status_t launch_gemm(const LinearDesc& d, const Ctx& c) {
     // HBM: 907 -> 992 TFLOP/s over 4 waves of 128 x 128); the DMA kernel also takes
     // fewer tiles than CUs, split in K, once each CU gets at least 16 slices of work, or,
     // for plain products with K >= 2048, 8 slices, or with K >= 4096 whenever 128 x 128
-    // tiles would leave half the CUs idle (70B QKV shard at 1024 / 512 tokens: 89 / 95 us
-    // on 80 / 40 register-staged 128 x 128 tiles). Short K stays off the split: its pieces
-    // cannot pay for the partials (O shard at 1024 tokens, K = 1024: 28 us as 512
-    // register-staged tiles, 47 us split). Otherwise register-staged 256 x 256 or
-    // 128 x 128 tiles.
+    // tiles would leave half the CUs idle (measured on the 70B QKV shard at 1024 / 512
+    // tokens: 89 / 95 us on 80 / 40 register-staged 128 x 128 tiles, 42 / 40 us split; that
+    // shard now takes the 160 x 128 tiles, which come first for plain products whose tiles,
+    // whole or cut in K, fill the chip). Short K stays off the split: its pieces cannot pay
+    // for the partials (O shard at 1024 tokens, K = 1024: 28 us as 512 register-staged
+    // tiles, 47 us split). Otherwise register-staged 256 x 256 or 128 x 128 tiles.
     const bool dma = d.K % DBK == 0;
     const int64_t kt = d.K / DBK;
     // Decode shapes that gemm_takes_decode accepts: 64-token tiles of 128 features (SwiGLU: 64
