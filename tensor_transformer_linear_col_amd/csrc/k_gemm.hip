@@ -700,7 +700,7 @@ __global__ __launch_bounds__(WAVES_N* WAVES_M * 64) void splitk_reduce_kernel(Ge
 // fp32 partial tiles summed in K order by splitk16_reduce_kernel, the next launch on the
 // stream (2048 tokens: 2 ranges, a third of the partials of 256 x 256 tiles in 6).
 //
-// The same kernel takes up to 64 tokens as one 64-token tile (SK): 128-feature tiles (64
+// The same kernel takes up to 64 tokens as one 64-token tile (SK): 128-feature tiles (96
 // SwiGLU pairs), each cut into K ranges the same way, a 4-deep DMA ring so that every CU
 // keeps its weight stream in flight; or whole-K tiles of 32 pairs in a 10-deep ring. The
 // tokens are staged once per slice for the 4 waves (the decode kernel's waves each reload
@@ -1017,13 +1017,13 @@ tp_status_t run_dtl16_bias(const LinearDesc& d, const Ctx& c) {
     return bias ? run_dtl16<TN, TM, true, float>(d, c) : run_dtl16<TN, TM, false, float>(d, c);
 }
 
-// Ring depth of the decode tiles: 4 slices of 32 KB (128 x 64 tiles, 64 SwiGLU pairs x 64;
-// a fifth measured no faster), else as many as the LDS holds, at most 10 (32 pairs x 64 tokens:
-// 10 x 16 KB).
+// Ring depth of the decode tiles: 4 slices of 32 KB (128 x 64 tiles; a fifth measured no
+// faster), 3 of 48 KB (96 SwiGLU pairs x 64 tokens), else as many as the LDS holds, at most 10
+// (32 pairs x 64 tokens: 10 x 16 KB).
 template <int TN, int TM, bool SW>
 constexpr int dtl16_decode_stages() {
     constexpr int b = Dtl16Shape<TN, TM, SW>::ROWS * Dtl16Shape<TN, TM, SW>::ROWB;
-    return b >= 32 * 1024 ? 4 : ((160 * 1024) / b > 10 ? 10 : (160 * 1024) / b);
+    return b >= 32 * 1024 ? ((160 * 1024) / b < 4 ? (160 * 1024) / b : 4) : ((160 * 1024) / b > 10 ? 10 : (160 * 1024) / b);
 }
 
 // Up to 64 tokens: every tile cut into S K ranges (S pieces per tile fill at most one wave of
@@ -1285,12 +1285,14 @@ tp_status_t launch_gemm(const LinearDesc& d, const Ctx& c) {
     // tiles, 47 us split). Otherwise register-staged 256 x 256 or 128 x 128 tiles.
     const bool dma = d.K % DBK == 0;
     const int64_t kt = d.K / DBK;
-    // Decode shapes that gemm_takes_decode accepts: 64-token tiles of 128 features (SwiGLU: 64
-    // pairs) per piece, K cut so that the pieces fill the chip, or whole-K tiles of 32 pairs.
+    // Decode shapes that gemm_takes_decode accepts: 64-token tiles of 128 features (SwiGLU: 96
+    // pairs; 7B TP=2 gate/up at 64 tokens 25.4 -> 24.1 us against 64 pairs, whose 86 tiles x 2
+    // K ranges filled 172 CUs) per piece, K cut so that the pieces fill the chip, or whole-K
+    // tiles of 32 pairs.
     if (d.M <= 64) {
         if (!gemm_takes_decode(d)) return TP_ERR_SHAPE;  // the decode kernels' shapes
         if (swiglu_pairs32(d, cus)) return run_dtl16_split_bias<32, 64, kActSwiglu>(d, cus, c);
-        if (d.swiglu) return run_dtl16_split_bias<64, 64, kActSwiglu>(d, cus, c);
+        if (d.swiglu) return run_dtl16_split_bias<96, 64, kActSwiglu>(d, cus, c);
         return run_dtl16_split_bias<128, 64, kActNone>(d, cus, c);
     }
     if (d.swiglu) {
