@@ -108,9 +108,12 @@ class SmallLayer:
 
 # Decode: 6 tokens, hidden 1024, 16 / 4 heads of 64, intermediate 2816 at TP = 4 (the QKV and
 # gate/up products cut K across workgroups: partial tiles and arrival counters).
+# Decode at 64 tokens: hidden 4096, 32 / 8 heads of 128, intermediate 11008 at TP = 2 (every
+# product on LDS-staged 64-token tiles whose K ranges meet in a reduce pass).
 # Prefill: 2048 tokens, the 70B attention shapes at TP = 8 with intermediate 4096 (the QKV
 # and gate/up products run split-K with a reduce pass).
-GRAPH_LAYERS = {"decode": (6, 1024, 2816, 16, 4, 64, 4), "prefill": (2048, 8192, 4096, 64, 8, 128, 8)}
+GRAPH_LAYERS = {"decode": (6, 1024, 2816, 16, 4, 64, 4), "decode64": (64, 4096, 11008, 32, 8, 128, 2),
+                "prefill": (2048, 8192, 4096, 64, 8, 128, 8)}
 
 
 @pytest.mark.parametrize("kind", list(GRAPH_LAYERS))
@@ -119,7 +122,7 @@ def test_layer_step_replays_under_graph_capture(kind):
     L = SmallLayer(*GRAPH_LAYERS[kind])
     with tp.tp_plan() as need:
         L.step()
-    assert need.partial_bytes > 0  # both sizes exercise a split reduction
+    assert need.partial_bytes > 0  # every size exercises a split reduction
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
         tp.tp_workspace_reserve(need.partial_bytes, need.n_counters)
